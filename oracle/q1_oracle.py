@@ -1,0 +1,300 @@
+"""CPU oracle for the packed Q1 (1-bit affine, group 128) decode path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library imports, links or calls this
+module; only the tests, the smoke check and the benchmark's CPU-baseline leg do.
+It shares no code with the HIP path: every step below is written from the
+pages' description of the format and from the plain definition of the
+operation, in NumPy, slowly and visibly.
+
+What it computes and where that is defined
+------------------------------------------
+* Packing (rMLX issue #207, "The good news -- packing is standard"): weights
+  are stored 32 per uint32 word; the Cactus PR #775 commit notes call it the
+  "linear LSB layout".  Weight ``k`` of a row is bit ``k & 31`` of word
+  ``k >> 5`` (least significant bit first).
+* Groups (same passage; mlx-gen backlog 0004, "Context"): one scale (and, for
+  affine tensors, one bias) per 128 consecutive weights along K, stored as
+  fp16 or bf16.
+* Affine dequantisation (Higgs PR #212, "What" and "Why"):
+  ``w = scale * bit + bias``.
+* Symmetric tensors (Higgs PR #212, "What": bias derived as ``-scale / 2``;
+  rMLX #207: bit 0 -> ``-s_g``, bit 1 -> ``+s_g``): the bias is not stored and
+  ``bias = -scale / 2``, so the two codes map to ``-scale/2`` and ``+scale/2``
+  (the pages' ``s_g`` is half the stored scale).  The halving is done in fp32,
+  where it is exact.
+* Narrow/wide matmul (Higgs PR #212, "What", "Validation"): ``y = x W^T`` over
+  the flattened leading dimensions of ``x``; the validation compares the packed
+  result with a matmul against the densely dequantised matrix -- which is what
+  :func:`qmm_ref` does, in fp64.
+* Fused dense FFN (Higgs PR #212, "What"): gate and up projections, then
+  ``SiLU(gate) * up``, then the down projection.
+
+Readings of the pages taken here (each also listed in the design notes):
+the dequantised weight is ``fl32(fl32(s * bit) + b)`` (one rounding, the add);
+outputs of dequantisation and gathering are rounded to the output dtype with
+round-to-nearest-even; the FFN keeps gate/up in full precision and rounds the
+hidden activation ``h`` once to bf16 before the down projection; token ids
+outside ``[0, V)`` give an all-zero row.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against values
+fixed by the format or by mathematics (hand-worked fixtures, closed forms,
+exact rational brute force, library routines).  No function is left unpinned.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+from typing import Optional
+
+import numpy as np
+
+GROUP = 128
+
+# --------------------------------------------------------------------------
+# Scalar formats (bit patterns in, float32 out; float32 in, bit patterns out)
+# --------------------------------------------------------------------------
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float32, exact: the bf16 pattern is the
+    upper half of the float32 pattern."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32)
+
+
+def f16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns -> float32 (exact widening)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def meta_to_f32(bits: np.ndarray, meta: str) -> np.ndarray:
+    if meta == "f16":
+        return f16_to_f32(bits)
+    if meta == "bf16":
+        return bf16_to_f32(bits)
+    raise ValueError(meta)
+
+
+def f32_to_bf16_rne(values: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest, ties to even.
+
+    Keep the upper 16 bits after adding ``0x7FFF`` plus the lowest kept bit:
+    below half an ulp rounds down, above rounds up, an exact tie rounds to the
+    even neighbour.  NaN inputs are quieted instead (never produced here).
+    """
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    u = v.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint32) & np.uint32(0xFFFF)
+    nan = np.isnan(v)
+    if nan.any():
+        r = np.where(nan, ((u >> np.uint64(16)).astype(np.uint32) | np.uint32(0x40)) & np.uint32(0xFFFF), r)
+    return r.astype(np.uint16)
+
+
+def f32_to_f16_rne(values: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE binary16 bit patterns; NumPy's conversion is the IEEE
+    round-to-nearest-even one."""
+    with np.errstate(over="ignore"):   # overflow to +-inf is the IEEE result
+        return np.ascontiguousarray(values, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def round_to(values_f32: np.ndarray, out_dtype: str) -> np.ndarray:
+    """Round float32 values to ``out_dtype``; returns uint16 bit patterns for
+    bf16/f16 and float32 values for f32."""
+    if out_dtype == "bf16":
+        return f32_to_bf16_rne(values_f32)
+    if out_dtype == "f16":
+        return f32_to_f16_rne(values_f32)
+    if out_dtype == "f32":
+        return np.ascontiguousarray(values_f32, dtype=np.float32)
+    raise ValueError(out_dtype)
+
+
+def out_to_f64(values: np.ndarray, out_dtype: str) -> np.ndarray:
+    """Stored output (bit patterns or float32) -> float64."""
+    if out_dtype == "bf16":
+        return bf16_to_f32(values).astype(np.float64)
+    if out_dtype == "f16":
+        return f16_to_f32(values).astype(np.float64)
+    return np.asarray(values, dtype=np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Unpacking and dequantisation
+# --------------------------------------------------------------------------
+
+
+def unpack_bits(packed: np.ndarray, K: int) -> np.ndarray:
+    """``[N, K/32]`` uint32 -> ``[N, K]`` uint8 codes; weight ``k`` is bit
+    ``k & 31`` of word ``k >> 5`` (LSB first)."""
+    packed = np.asarray(packed, dtype=np.uint32)
+    k = np.arange(K)
+    words = packed[:, k >> 5]
+    return ((words >> (k & 31).astype(np.uint32)) & np.uint32(1)).astype(np.uint8)
+
+
+def group_scale_bias(scales: np.ndarray, biases: Optional[np.ndarray], meta: str,
+                     symmetric: bool) -> tuple[np.ndarray, np.ndarray]:
+    """Per-group fp32 scale and bias ``[N, G]``.  Symmetric: ``b = -0.5 * s``
+    computed in fp32 (exact)."""
+    s = meta_to_f32(scales, meta)
+    if symmetric:
+        if biases is not None:
+            raise ValueError("symmetric tensors carry no stored bias")
+        b = (np.float32(-0.5) * s).astype(np.float32)
+    else:
+        if biases is None:
+            raise ValueError("affine tensors need a stored bias")
+        b = meta_to_f32(biases, meta)
+    return s, b
+
+
+def dequant_f32(packed: np.ndarray, scales: np.ndarray, biases: Optional[np.ndarray], meta: str,
+                symmetric: bool, K: int) -> np.ndarray:
+    """Dense float32 weights ``[N, K]``: ``w = fl32(fl32(s * bit) + b)``."""
+    bits = unpack_bits(packed, K).astype(np.float32)
+    s, b = group_scale_bias(scales, biases, meta, symmetric)
+    g = np.arange(K) // GROUP
+    sk = s[:, g]
+    bk = b[:, g]
+    prod = (sk * bits).astype(np.float32)       # exact: bit is 0 or 1
+    return (prod + bk).astype(np.float32)       # the one rounding
+
+
+def dequantize(packed, scales, biases, meta, symmetric, K, out_dtype):
+    """Dequantised matrix rounded to ``out_dtype`` (bit patterns for 16-bit
+    types, float32 values for f32)."""
+    return round_to(dequant_f32(packed, scales, biases, meta, symmetric, K), out_dtype)
+
+
+def embed_rows(ids: np.ndarray, packed, scales, biases, meta, symmetric, K, out_dtype):
+    """Rows ``ids`` of the dequantised table, rounded to ``out_dtype``; an id
+    outside ``[0, V)`` yields a row of zeros."""
+    ids = np.asarray(ids).astype(np.int64)
+    V = packed.shape[0]
+    ok = (ids >= 0) & (ids < V)
+    safe = np.where(ok, ids, 0)
+    rows = dequant_f32(packed[safe], scales[safe], None if biases is None else biases[safe], meta, symmetric, K)
+    rows[~ok] = 0.0
+    return round_to(rows, out_dtype)
+
+
+# --------------------------------------------------------------------------
+# Matmul reference and tolerance
+# --------------------------------------------------------------------------
+
+
+def qmm_ref(x_bits: np.ndarray, packed, scales, biases, meta, symmetric, K, block_rows: int = 4096,
+            row_index: Optional[np.ndarray] = None):
+    """``y = x W^T`` in fp64 plus ``A = |x| |W|^T`` (for the tolerance).
+
+    ``x_bits``: bf16 bit patterns ``[..., K]``; leading dims are flattened to M
+    rows and restored on the output.  ``row_index`` restricts the output
+    columns to the given weight rows (for sampled checks of large matrices).
+    Returns ``(y, A)`` of shape ``[..., n_out]``.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    lead = x_bits.shape[:-1]
+    x = bf16_to_f32(x_bits.reshape(-1, K)).astype(np.float64)
+    rows = np.arange(packed.shape[0]) if row_index is None else np.asarray(row_index, dtype=np.int64)
+    M = x.shape[0]
+    y = np.empty((M, rows.size), dtype=np.float64)
+    A = np.empty((M, rows.size), dtype=np.float64)
+    ax = np.abs(x)
+    for r0 in range(0, rows.size, block_rows):
+        sel = rows[r0:r0 + block_rows]
+        w = dequant_f32(packed[sel], scales[sel], None if biases is None else biases[sel], meta, symmetric,
+                        K).astype(np.float64)
+        y[:, r0:r0 + sel.size] = x @ w.T
+        A[:, r0:r0 + sel.size] = ax @ np.abs(w).T
+    return y.reshape(*lead, rows.size), A.reshape(*lead, rows.size)
+
+
+def tolerance(A: np.ndarray) -> np.ndarray:
+    """Per-element bound on ``|y - y_ref|``: ``1e-3 * sum_k |w_nk x_k| + 1e-6``."""
+    return 1e-3 * np.asarray(A, dtype=np.float64) + 1e-6
+
+
+def check_close(y_stored: np.ndarray, out_dtype: str, y_ref: np.ndarray, A: np.ndarray):
+    """Returns ``(ok, worst err/bound ratio, number of violations)``."""
+    y = out_to_f64(y_stored, out_dtype)
+    err = np.abs(y - y_ref)
+    bound = tolerance(A)
+    ratio = err / bound
+    return bool((err <= bound).all()), float(ratio.max(initial=0.0)), int((err > bound).sum())
+
+
+def qmm_exact(x_bits: np.ndarray, packed, scales, biases, meta, symmetric, K) -> list:
+    """Exact rational ``x W^T`` for tiny inputs (pure-Python ``Fraction``s of
+    the bf16 activations and the fp32 dequantised weights)."""
+    x = bf16_to_f32(np.asarray(x_bits, dtype=np.uint16).reshape(-1, K))
+    w = dequant_f32(packed, scales, biases, meta, symmetric, K)
+    out = []
+    for m in range(x.shape[0]):
+        row = []
+        for n in range(w.shape[0]):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(float(x[m, k])) * Fraction(float(w[n, k]))
+            row.append(acc)
+        out.append(row)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Fused dense FFN
+# --------------------------------------------------------------------------
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """``z * sigmoid(z) = z / (1 + exp(-z))`` in fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def ffn_ref(x_bits: np.ndarray, gate: dict, up: dict, down: dict):
+    """Reference for ``y = (SiLU(x Wg^T) * (x Wu^T)) Wd^T``.
+
+    Each weight is a dict with keys packed, scales, biases, meta, symmetric, K.
+    Returns a dict with the fp64 gate/up products, their tolerance sums, the
+    fp64 hidden activation ``h64``, its bf16 rounding ``hb`` (bit patterns),
+    and ``y_ref = hb Wd^T`` with ``A_d = |hb| |Wd|^T``.
+    """
+    g, Ag = qmm_ref(x_bits, **gate)
+    u, Au = qmm_ref(x_bits, **up)
+    h64 = silu(g) * u
+    hb = f32_to_bf16_rne(h64.astype(np.float32))
+    y, Ad = qmm_ref(hb, **down)
+    return {"g": g, "Ag": Ag, "u": u, "Au": Au, "h64": h64, "hb": hb, "y": y, "Ad": Ad}
+
+
+def ffn_h_bound(ref: dict) -> np.ndarray:
+    """Allowed ``|h_gpu - h64|``: first-order propagation of the gate/up
+    tolerances through ``SiLU(g) * u`` plus one bf16 rounding of ``h`` (half
+    an ulp, taken as 2^-8 relative to be safe), plus 1e-6."""
+    g, u = ref["g"], ref["u"]
+    dg = tolerance(ref["Ag"])
+    du = tolerance(ref["Au"])
+    prop = np.abs(silu_grad(g)) * np.abs(u) * dg + np.abs(silu(g)) * du + dg * du
+    return prop + np.abs(ref["h64"]) * 2.0 ** -8 + 1e-6
+
+
+def ffn_y_bound(ref: dict, down: dict) -> np.ndarray:
+    """Allowed ``|y_gpu - y_ref|`` end to end: the down projection's own
+    tolerance plus ``sum_j |Wd_nj| * dh_j``, where ``dh`` bounds the
+    difference between the GPU's rounded ``h`` and the reference's ``hb``."""
+    # the GPU's bf16 h and the reference's bf16 h each carry one rounding
+    dh = ffn_h_bound(ref) + np.abs(ref["h64"]) * 2.0 ** -8
+    wd = np.abs(dequant_f32(down["packed"], down["scales"], down["biases"], down["meta"], down["symmetric"],
+                            down["K"]).astype(np.float64))
+    lead = dh.shape[:-1]
+    prop = dh.reshape(-1, dh.shape[-1]) @ wd.T
+    return tolerance(ref["Ad"]) + prop.reshape(*lead, wd.shape[0])
