@@ -1,0 +1,110 @@
+// Internal interface between the C ABI (q1_api.cpp) and the HIP kernels
+// (q1_kernels.hip).  Not installed; not part of the public boundary.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace q1 {
+
+enum Dtype : int32_t { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Weight rows per packed-kernel chunk: 32 words = 1024 weights along K.
+constexpr int kChunkWords = 32;
+constexpr int kChunkK = 1024;
+// Bytes of lookup table per (chunk, activation row).
+constexpr int kTabBytes = 16384;
+// Threads per packed-kernel workgroup: 16 waves for one activation row
+// (small register footprint, two workgroups per CU share the LDS), 8 waves
+// otherwise.
+constexpr int gemv_threads(int M) { return M == 1 ? 1024 : 512; }
+// Chunks of K one workgroup covers (its lookup tables must fit in LDS).
+constexpr int gemv_krmax(int M) { return M == 1 ? 5 : M == 2 ? 2 : 1; }
+// LDS bytes between the tables of consecutive chunks (a chunk's M tables never
+// straddle a 64 KB window).
+constexpr int gemv_chunk_block(int M) { return M == 1 ? 16384 : M == 2 ? 32768 : M <= 4 ? 65536 : 131072; }
+constexpr int gemv_lds_bytes(int M) { return (gemv_krmax(M) - 1) * gemv_chunk_block(M) + M * 16384; }
+// Bytes at the start of every workspace reserved for arrival counters
+// (Q1_WS_RESERVED_BYTES in the public header).
+constexpr int kCounterBytes = 16384;
+
+struct QMat {
+  const uint32_t* packed;
+  const uint16_t* scales;
+  const uint16_t* biases;  // null when symmetric
+  int32_t meta_bf16;       // 1: bf16 metadata, 0: fp16
+  int32_t symmetric;
+  int64_t N, K;
+};
+
+// Plan of one packed launch (chosen on the host, see plan_gemv).
+struct GemvPlan {
+  int M;
+  int chunks;   // ceil(K / 1024)
+  int KS;       // K splits (grid.y)
+  int KR;       // chunks per split (the last split may have fewer)
+  int64_t units;         // N (single) or 2N (gate/up pair)
+  int64_t units_per_wg;  // even
+  int wgs_x;             // grid.x
+  int threads;           // workgroup size
+  int exact;             // every K range has exactly gemv_krmax(M) full chunks
+  size_t lds_bytes;
+  size_t partial_floats;  // KS > 1: KS*M*units
+  size_t counters;        // KS > 1: wgs_x
+};
+
+// Kernel arguments of one packed launch.
+struct GemvArgs {
+  const uint16_t* x;
+  int64_t x_ld;
+  const uint32_t* p0;
+  const uint32_t* p1;
+  const uint16_t* s0;
+  const uint16_t* s1;
+  const uint16_t* b0;
+  const uint16_t* b1;
+  int64_t N;
+  int32_t K, wpr, gpr, chunks;
+  int32_t KS, pair;
+  int32_t full_chunks;   // chunks with all 32 words inside the row (K / 1024)
+  int32_t fused_splitk;  // 1: finish split-K in the kernel (arrival counters)
+  int64_t units, units_per_wg;
+  uint32_t packed_bytes;  // N * K / 8      (< 2^31)
+  uint32_t meta_bytes;    // N * K / 128 * 2 (< 2^31)
+  int32_t out_dtype;
+  void* out;
+  int64_t out_ld;
+  float* partial;
+  uint32_t* counters;
+};
+
+// Launch the packed kernel for M activation rows (defined in q1_gemv_m<M>.hip).
+template <int M>
+hipError_t launch_gemv_m(const GemvPlan& plan, const GemvArgs& args, bool affine, bool mbf16, hipStream_t stream);
+
+// Returns false (with a message) when the request cannot be planned.
+bool plan_gemv(int M, int64_t N, int64_t K, bool pair, bool affine, GemvPlan* plan, const char** why);
+
+// y (single) or h (pair) from packed weights.  `a` is the matrix for single
+// mode and gate for pair mode; `b` is up (pair mode) or ignored.
+// out_dtype: F32/BF16/F16 for single mode; pair mode always writes bf16 h.
+// partial/counters: workspace regions sized by the plan (may be null if KS==1).
+hipError_t launch_gemv(const GemvPlan& plan, const uint16_t* x, int64_t x_ld, const QMat& a, const QMat* b,
+                       void* out, int32_t out_dtype, int64_t out_ld, float* partial, uint32_t* counters,
+                       hipStream_t stream);
+
+// Dequantise rows of `w` into out[T, K] (row r of the output is weight row
+// rows[r], or r when rows is null).  ids may be int32 or int64.
+hipError_t launch_dequant(const QMat& w, const void* ids, int ids_int64, int64_t T, void* out, int32_t out_dtype,
+                          hipStream_t stream);
+
+// y[M, N] (bf16 or fp32) = x[M, K] (bf16) * B[N, K]^T (bf16), fp32 accumulate.
+hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* B, int64_t M, int64_t N, int64_t K, void* y,
+                            int32_t y_dtype, hipStream_t stream);
+
+// h[i] = bf16(SiLU(g[i]) * u[i]) for fp32 g, u (n elements).
+hipError_t launch_silu_mul(const float* g, const float* u, uint16_t* h, int64_t n, hipStream_t stream);
+
+}  // namespace q1

@@ -1,0 +1,151 @@
+/*
+ * q1.h -- C ABI of the packed Q1 (1-bit affine, group 128) decode library for
+ * AMD MI355X (gfx950).
+ *
+ * Format (rMLX issue #207, "The good news -- packing is standard"; Cactus PR
+ * #775, commit notes, "linear LSB layout"; mlx-gen backlog 0004, "Context"):
+ *   packed  uint32 [N, K/32], row-major; weight k of row n is bit (k & 31) of
+ *           word (k >> 5) (least significant bit first);
+ *   scales  fp16 or bf16 [N, K/128], row-major, one per 128 weights along K;
+ *   biases  same shape and dtype, or NULL for a symmetric tensor.
+ * Dequantisation (Higgs PR #212, "What", "Why"): w = scale * bit + bias; a
+ * symmetric tensor derives bias = -scale/2 (computed in fp32, exact), so its
+ * codes map to -scale/2 and +scale/2.  The dequantised value is
+ * fl32(fl32(scale * bit) + bias) -- a single rounding.
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are caller-owned device memory, contiguous and
+ *     row-major.  The library keeps no reference after a call returns and never
+ *     allocates device memory; temporaries live in a caller workspace.
+ *   - Every call validates its arguments before any HIP call and returns
+ *     Q1_ERR_INVALID_ARG / Q1_ERR_UNSUPPORTED / Q1_ERR_WORKSPACE with a short
+ *     message in q1_last_error() (thread-local).  Q1_ERR_HIP reports a failed
+ *     launch.  Kernel faults surface at the caller's next synchronisation.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work on it and return.
+ *   - Rounding of every stored result is round-to-nearest-even; subnormals are
+ *     kept.
+ */
+#ifndef Q1_H
+#define Q1_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum q1_status {
+  Q1_OK = 0,
+  Q1_ERR_INVALID_ARG = 1, /* a shape, pointer, dtype or flag is wrong */
+  Q1_ERR_UNSUPPORTED = 2, /* valid request this build does not serve (e.g. not gfx950) */
+  Q1_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the *_workspace_bytes query */
+  Q1_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} q1_status;
+
+typedef enum q1_dtype { Q1_F32 = 0, Q1_F16 = 1, Q1_BF16 = 2 } q1_dtype;
+
+/* The first Q1_WS_RESERVED_BYTES bytes of every workspace hold split-K
+ * arrival counters.  They must be zero before a workspace is first used; every
+ * call leaves them zero again once the stream has executed it, and no call
+ * writes anything else there.  All other temporaries start after them. */
+#define Q1_WS_RESERVED_BYTES 16384
+
+/* One packed Q1 matrix (caller-owned device memory). */
+typedef struct q1_weight {
+  const uint32_t* packed; /* [N, K/32]; 4-byte aligned */
+  const void* scales;     /* [N, K/128], meta_dtype */
+  const void* biases;     /* [N, K/128], meta_dtype; NULL iff symmetric */
+  int32_t meta_dtype;     /* Q1_F16 or Q1_BF16 */
+  int32_t symmetric;      /* 1: bias = -scale/2 derived in-kernel (biases must be NULL) */
+  int64_t N;              /* rows (output features) */
+  int64_t K;              /* weights per row; K % 128 == 0 */
+  int32_t group_size;     /* must be 128 */
+  int32_t reserved;       /* must be 0 */
+} q1_weight;
+
+/*
+ * q1_qmm -- y[M, N] = x[M, K] . W^T  (Higgs PR #212, "What": packed Q1 linear
+ * and tied head; "Limitations": wider forwards use the dense fallback).
+ *   x        bf16 [M, K] (M = product of the caller's leading dims)
+ *   x_dtype  must be Q1_BF16
+ *   w        the packed matrix (N, K)
+ *   y        [M, N] in y_dtype (Q1_F32, Q1_BF16 or Q1_F16)
+ *   M <= max packed rows (default 8): packed narrow-M kernel, fp32
+ *     accumulation, one rounding to y_dtype.
+ *   M  > max packed rows: the matrix is dequantised to bf16 in the workspace,
+ *     then a bf16 MFMA GEMM with fp32 accumulation runs.
+ *   workspace  device memory of at least q1_qmm_workspace_bytes(M, w) bytes,
+ *     256-byte aligned (may be NULL when that query returns 0).  Its first
+ *     Q1_WS_RESERVED_BYTES must be zero (see above).  Calls that share one
+ *     workspace must be ordered (same stream); concurrent calls need separate
+ *     workspaces.
+ */
+q1_status q1_qmm(const void* x, int32_t x_dtype, int64_t M, const q1_weight* w, void* y, int32_t y_dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes q1_qmm needs for these shapes (0 is a valid answer only if
+ * the call needs none).  Returns 0 and sets q1_last_error() on invalid input. */
+size_t q1_qmm_workspace_bytes(int64_t M, const q1_weight* w);
+
+/*
+ * q1_dequantize -- out[N, K] = round(fl32(fl32(scale*bit) + bias)), bit-exact
+ * (Higgs PR #212, "Walkthrough": Q1 dequantization kernel; rMLX #207,
+ * "Current behavior": the affine_dequantize_bfloat16 kernel upstream lacks).
+ *   out_dtype  Q1_BF16, Q1_F16 or Q1_F32.
+ */
+q1_status q1_dequantize(const q1_weight* w, void* out, int32_t out_dtype, void* stream);
+
+/*
+ * q1_embed_rows -- out[t, :] = dequantised row ids[t] of the table, rounded to
+ * out_dtype, bit-exact; an id outside [0, N) writes a row of zeros (Higgs PR
+ * #212, "What": embedding routed through the Q1 kernels).
+ *   ids            device int32 [T] (ids_are_int64 = 0) or int64 [T] (= 1)
+ *   out            [T, K] in out_dtype (Q1_BF16, Q1_F16 or Q1_F32)
+ */
+q1_status q1_embed_rows(const void* ids, int32_t ids_are_int64, int64_t T, const q1_weight* table, void* out,
+                        int32_t out_dtype, void* stream);
+
+/*
+ * q1_ffn -- fused dense FFN, y = (SiLU(x Wg^T) * (x Wu^T)) Wd^T (Higgs PR #212,
+ * "What": fused dense-FFN operations; the SiLU-times-up form is the standard
+ * gated FFN of the Qwen3.5 family).
+ *   x      bf16 [M, H], H = gate.K = up.K
+ *   gate, up   [I, H];  down [H_out, I]  (down.K == gate.N == up.N)
+ *   y      bf16 [M, H_out]
+ *   Gate and up accumulate in fp32; h = SiLU(g)*u is rounded once to bf16 and
+ *   is left in the workspace at byte offset Q1_WS_RESERVED_BYTES (bf16 [M, I]).
+ *   M <= max packed rows: gate+up in one packed launch with the SiLU*mul
+ *   epilogue (when gate and up share metadata dtype and symmetry; otherwise
+ *   two packed launches and an element-wise kernel), then the packed down
+ *   projection.  M > max packed rows: dequantise + MFMA GEMM per projection.
+ *   workspace  q1_ffn_workspace_bytes(...) bytes; same rules as for q1_qmm.
+ */
+q1_status q1_ffn(const void* x, int64_t M, const q1_weight* gate, const q1_weight* up, const q1_weight* down,
+                 void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t q1_ffn_workspace_bytes(int64_t M, const q1_weight* gate, const q1_weight* up, const q1_weight* down);
+
+/* Largest M served by the packed kernel (1..8, default 8, initial value from
+ * the environment variable Q1_QMM_MAX_ROWS).  Returns the previous value, or
+ * -1 (value unchanged) when rows is outside 1..8.  (Higgs PR #212,
+ * "Limitations": the packed-rows threshold is a tuning override.) */
+int q1_set_max_packed_rows(int rows);
+
+/* Q1_OK if `device` is a gfx950 GPU; Q1_ERR_UNSUPPORTED with a message
+ * otherwise (mlx-gen backlog 0004: fail early with an explicit message when
+ * the runtime cannot execute 1-bit kernels). */
+q1_status q1_device_supported(int device);
+
+/* Text of the last error on this thread ("" if none).  Static storage. */
+const char* q1_last_error(void);
+
+/* Library version string. */
+const char* q1_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q1_H */

@@ -185,12 +185,15 @@ def embed_rows(ids: np.ndarray, packed, scales, biases, meta, symmetric, K, out_
 
 
 def qmm_ref(x_bits: np.ndarray, packed, scales, biases, meta, symmetric, K, block_rows: int = 4096,
-            row_index: Optional[np.ndarray] = None):
+            row_index: Optional[np.ndarray] = None, weights_bf16: bool = False):
     """``y = x W^T`` in fp64 plus ``A = |x| |W|^T`` (for the tolerance).
 
     ``x_bits``: bf16 bit patterns ``[..., K]``; leading dims are flattened to M
     rows and restored on the output.  ``row_index`` restricts the output
     columns to the given weight rows (for sampled checks of large matrices).
+    ``weights_bf16``: the dense fallback for wide M (Higgs PR #212,
+    "Limitations": wider forwards dequantise to the input dtype, bf16 here,
+    before the dense matmul) -- W is rounded to bf16 before the product.
     Returns ``(y, A)`` of shape ``[..., n_out]``.
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
@@ -203,11 +206,19 @@ def qmm_ref(x_bits: np.ndarray, packed, scales, biases, meta, symmetric, K, bloc
     ax = np.abs(x)
     for r0 in range(0, rows.size, block_rows):
         sel = rows[r0:r0 + block_rows]
-        w = dequant_f32(packed[sel], scales[sel], None if biases is None else biases[sel], meta, symmetric,
-                        K).astype(np.float64)
+        w = dequant_f32(packed[sel], scales[sel], None if biases is None else biases[sel], meta, symmetric, K)
+        if weights_bf16:
+            w = bf16_to_f32(f32_to_bf16_rne(w))
+        w = w.astype(np.float64)
         y[:, r0:r0 + sel.size] = x @ w.T
         A[:, r0:r0 + sel.size] = ax @ np.abs(w).T
     return y.reshape(*lead, rows.size), A.reshape(*lead, rows.size)
+
+
+def dense_rounding_bound(A: np.ndarray) -> np.ndarray:
+    """Bound on ``|x W_bf16^T - x W^T|``: each weight moves by at most half a
+    bf16 ulp, i.e. ``2^-8 |w|``, so the product moves by at most ``2^-8 A``."""
+    return np.asarray(A, dtype=np.float64) * 2.0 ** -8
 
 
 def tolerance(A: np.ndarray) -> np.ndarray:
@@ -224,11 +235,14 @@ def check_close(y_stored: np.ndarray, out_dtype: str, y_ref: np.ndarray, A: np.n
     return bool((err <= bound).all()), float(ratio.max(initial=0.0)), int((err > bound).sum())
 
 
-def qmm_exact(x_bits: np.ndarray, packed, scales, biases, meta, symmetric, K) -> list:
+def qmm_exact(x_bits: np.ndarray, packed, scales, biases, meta, symmetric, K, weights_bf16: bool = False) -> list:
     """Exact rational ``x W^T`` for tiny inputs (pure-Python ``Fraction``s of
-    the bf16 activations and the fp32 dequantised weights)."""
+    the bf16 activations and the fp32 dequantised weights, or of their bf16
+    roundings with ``weights_bf16``)."""
     x = bf16_to_f32(np.asarray(x_bits, dtype=np.uint16).reshape(-1, K))
     w = dequant_f32(packed, scales, biases, meta, symmetric, K)
+    if weights_bf16:
+        w = bf16_to_f32(f32_to_bf16_rne(w))
     out = []
     for m in range(x.shape[0]):
         row = []
@@ -260,19 +274,20 @@ def silu_grad(z: np.ndarray) -> np.ndarray:
     return sg * (1.0 + z * (1.0 - sg))
 
 
-def ffn_ref(x_bits: np.ndarray, gate: dict, up: dict, down: dict):
+def ffn_ref(x_bits: np.ndarray, gate: dict, up: dict, down: dict, weights_bf16: bool = False):
     """Reference for ``y = (SiLU(x Wg^T) * (x Wu^T)) Wd^T``.
 
     Each weight is a dict with keys packed, scales, biases, meta, symmetric, K.
-    Returns a dict with the fp64 gate/up products, their tolerance sums, the
+    ``weights_bf16`` selects the wide-M (dense fallback) definition for all
+    three projections.  Returns a dict with the fp64 gate/up products, their tolerance sums, the
     fp64 hidden activation ``h64``, its bf16 rounding ``hb`` (bit patterns),
     and ``y_ref = hb Wd^T`` with ``A_d = |hb| |Wd|^T``.
     """
-    g, Ag = qmm_ref(x_bits, **gate)
-    u, Au = qmm_ref(x_bits, **up)
+    g, Ag = qmm_ref(x_bits, **gate, weights_bf16=weights_bf16)
+    u, Au = qmm_ref(x_bits, **up, weights_bf16=weights_bf16)
     h64 = silu(g) * u
     hb = f32_to_bf16_rne(h64.astype(np.float32))
-    y, Ad = qmm_ref(hb, **down)
+    y, Ad = qmm_ref(hb, **down, weights_bf16=weights_bf16)
     return {"g": g, "Ag": Ag, "u": u, "Au": Au, "h64": h64, "hb": hb, "y": y, "Ad": Ad}
 
 
@@ -287,14 +302,16 @@ def ffn_h_bound(ref: dict) -> np.ndarray:
     return prop + np.abs(ref["h64"]) * 2.0 ** -8 + 1e-6
 
 
-def ffn_y_bound(ref: dict, down: dict) -> np.ndarray:
+def ffn_y_bound(ref: dict, down: dict, weights_bf16: bool = False) -> np.ndarray:
     """Allowed ``|y_gpu - y_ref|`` end to end: the down projection's own
     tolerance plus ``sum_j |Wd_nj| * dh_j``, where ``dh`` bounds the
     difference between the GPU's rounded ``h`` and the reference's ``hb``."""
     # the GPU's bf16 h and the reference's bf16 h each carry one rounding
     dh = ffn_h_bound(ref) + np.abs(ref["h64"]) * 2.0 ** -8
-    wd = np.abs(dequant_f32(down["packed"], down["scales"], down["biases"], down["meta"], down["symmetric"],
-                            down["K"]).astype(np.float64))
+    wd = dequant_f32(down["packed"], down["scales"], down["biases"], down["meta"], down["symmetric"], down["K"])
+    if weights_bf16:
+        wd = bf16_to_f32(f32_to_bf16_rne(wd))
+    wd = np.abs(wd.astype(np.float64))
     lead = dh.shape[:-1]
     prop = dh.reshape(-1, dh.shape[-1]) @ wd.T
     return tolerance(ref["Ad"]) + prop.reshape(*lead, wd.shape[0])

@@ -398,3 +398,42 @@ def test_planted_transposed_operand_is_caught(monkeypatch):
         return y[..., ::-1].copy(), A[..., ::-1].copy()   # columns mixed up
     _patch(monkeypatch, "qmm_ref", transposed)
     assert not _pins_pass()
+
+
+# ---------------------------------------------------------------- dense fallback (bf16 weights)
+
+def test_dense_bf16_equals_exact_when_weights_are_bf16():
+    # bf16 symmetric metadata: +-scale/2 is itself a bf16 value, so rounding the
+    # dequantised matrix to bf16 changes nothing.
+    rng = np.random.Generator(np.random.PCG64(31))
+    w = S.draw_weight(rng, 40, 1024, "bf16", True)
+    x = S.draw_x(rng, 3, 1024)
+    a = O.qmm_ref(x, w.packed, w.scales, None, "bf16", True, 1024)
+    b = O.qmm_ref(x, w.packed, w.scales, None, "bf16", True, 1024, weights_bf16=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("symmetric,meta", [(True, "f16"), (False, "bf16")])
+def test_dense_bf16_bruteforce_and_bound(symmetric, meta):
+    rng = np.random.Generator(np.random.PCG64(32))
+    w = S.draw_weight(rng, 3, 256, meta, symmetric)
+    x = S.draw_x(rng, 2, 256)
+    y, A = O.qmm_ref(x, w.packed, w.scales, w.biases, meta, symmetric, 256, weights_bf16=True)
+    ex = O.qmm_exact(x, w.packed, w.scales, w.biases, meta, symmetric, 256, weights_bf16=True)
+    for m in range(2):
+        for n in range(3):
+            assert abs(Fraction(float(y[m, n])) - ex[m][n]) <= Fraction(float(A[m, n])) / 2 ** 45
+    y0, A0 = O.qmm_ref(x, w.packed, w.scales, w.biases, meta, symmetric, 256)
+    assert (np.abs(y - y0) <= O.dense_rounding_bound(A0)).all()
+    if meta == "f16":
+        assert not np.array_equal(y, y0)  # fp16-derived weights do move under bf16 rounding
+
+
+def test_planted_missing_bf16_rounding_is_caught(monkeypatch):
+    orig = O.q1_oracle.qmm_ref
+
+    def no_rounding(*args, weights_bf16=False, **kw):
+        return orig(*args, **kw)
+    _patch(monkeypatch, "qmm_ref", no_rounding)
+    with pytest.raises(AssertionError):
+        test_dense_bf16_bruteforce_and_bound(True, "f16")
