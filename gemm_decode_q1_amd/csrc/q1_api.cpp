@@ -114,20 +114,47 @@ q1_status hip_status(hipError_t e, const char* what) {
 // leave them zero); a packed launch's fp32 partial sums go at `base`.
 constexpr size_t kReserved = Q1_WS_RESERVED_BYTES;
 
+// Packed narrow-M launches: the nibble-table kernel (q1_gemv.inc) for one
+// activation row, the matrix-core kernel (q1_mma.hip) for 2..8 rows, where
+// table lookups grow with the row count.  Q1_PACKED_KERNEL=table|mma forces
+// one of them for every row count.
+bool use_table_kernel(int M) {
+  static const int v = [] {
+    const char* e = getenv("Q1_PACKED_KERNEL");
+    if (e && strcmp(e, "table") == 0) return 1;
+    if (e && strcmp(e, "mma") == 0) return 2;
+    return 0;
+  }();
+  return v == 1 || (v == 0 && M == 1);
+}
+
+struct PackedPlan {
+  bool table;
+  q1::GemvPlan g;
+  q1::MmaPlan m;
+  size_t partial_floats() const { return table ? (g.KS > 1 ? g.partial_floats : 0) : m.partial_floats; }
+};
+
+bool plan_packed(int M, int64_t N, int64_t K, bool pair, bool affine, PackedPlan* p, const char** why) {
+  p->table = use_table_kernel(M);
+  if (p->table) return q1::plan_gemv(M, N, K, pair, affine, &p->g, why);
+  return q1::plan_mma(M, N, K, pair, affine, &p->m, why);
+}
+
 struct PackedWs {
   size_t partial_off, bytes;  // bytes used from `base` on
 };
 
-PackedWs packed_ws(const q1::GemvPlan& p, size_t base) {
+PackedWs packed_ws(const PackedPlan& p, size_t base) {
   PackedWs w;
   w.partial_off = base;
-  w.bytes = (p.KS > 1) ? align_up(p.partial_floats * sizeof(float), 256) : 0;
+  w.bytes = align_up(p.partial_floats() * sizeof(float), 256);
   return w;
 }
 
 struct FfnWs {
   bool packed, fused;
-  q1::GemvPlan pgu, pg, pu, pd;
+  PackedPlan pgu, pg, pu, pd;
   size_t h_off, gu_off, d_off;     // packed: counters+partials blocks
   size_t g_off, u_off;             // unfused / wide: fp32 g and u
   size_t deq_off;                  // wide: dequantised matrix
@@ -147,13 +174,13 @@ q1_status ffn_layout(int64_t M, const q1_weight* gate, const q1_weight* up, cons
   const char* why = "";
   if (L->packed) {
     if (L->fused) {
-      if (!q1::plan_gemv((int)M, I, H, true, !gate->symmetric, &L->pgu, &why)) return fail(Q1_ERR_UNSUPPORTED, "%s", why);
+      if (!plan_packed((int)M, I, H, true, !gate->symmetric, &L->pgu, &why)) return fail(Q1_ERR_UNSUPPORTED, "%s", why);
       PackedWs w = packed_ws(L->pgu, off);
       L->gu_off = off;
       off += w.bytes;
     } else {
-      if (!q1::plan_gemv((int)M, I, H, false, !gate->symmetric, &L->pg, &why) ||
-          !q1::plan_gemv((int)M, up->N, up->K, false, !up->symmetric, &L->pu, &why))
+      if (!plan_packed((int)M, I, H, false, !gate->symmetric, &L->pg, &why) ||
+          !plan_packed((int)M, up->N, up->K, false, !up->symmetric, &L->pu, &why))
         return fail(Q1_ERR_UNSUPPORTED, "%s", why);
       L->g_off = off;
       off = align_up(off + (size_t)M * I * 4, 256);
@@ -163,7 +190,7 @@ q1_status ffn_layout(int64_t M, const q1_weight* gate, const q1_weight* up, cons
       PackedWs wg = packed_ws(L->pg, off), wu = packed_ws(L->pu, off);
       off += wg.bytes > wu.bytes ? wg.bytes : wu.bytes;
     }
-    if (!q1::plan_gemv((int)M, Ho, I, false, !down->symmetric, &L->pd, &why)) return fail(Q1_ERR_UNSUPPORTED, "%s", why);
+    if (!plan_packed((int)M, Ho, I, false, !down->symmetric, &L->pd, &why)) return fail(Q1_ERR_UNSUPPORTED, "%s", why);
     L->d_off = off;
     off += packed_ws(L->pd, off).bytes;
   } else {
@@ -180,12 +207,17 @@ q1_status ffn_layout(int64_t M, const q1_weight* gate, const q1_weight* up, cons
   return Q1_OK;
 }
 
-q1_status run_packed(const q1::GemvPlan& p, const uint16_t* x, int64_t x_ld, const q1::QMat& a, const q1::QMat* b,
+q1_status run_packed(const PackedPlan& p, const uint16_t* x, int64_t x_ld, const q1::QMat& a, const q1::QMat* b,
                      void* out, int32_t out_dtype, int64_t out_ld, unsigned char* ws, size_t base, hipStream_t s) {
   PackedWs w = packed_ws(p, base);
-  float* partial = p.KS > 1 ? reinterpret_cast<float*>(ws + w.partial_off) : nullptr;
-  uint32_t* counters = p.KS > 1 ? reinterpret_cast<uint32_t*>(ws) : nullptr;
-  return hip_status(q1::launch_gemv(p, x, x_ld, a, b, out, out_dtype, out_ld, partial, counters, s), "packed kernel launch");
+  const bool split = p.partial_floats() > 0;
+  float* partial = split ? reinterpret_cast<float*>(ws + w.partial_off) : nullptr;
+  uint32_t* counters = split ? reinterpret_cast<uint32_t*>(ws) : nullptr;
+  if (p.table)
+    return hip_status(q1::launch_gemv(p.g, x, x_ld, a, b, out, out_dtype, out_ld, partial, counters, s),
+                      "packed kernel launch");
+  return hip_status(q1::launch_mma(p.m, x, x_ld, a, b, out, out_dtype, out_ld, partial, counters, s),
+                    "packed kernel launch");
 }
 
 }  // namespace
@@ -225,9 +257,9 @@ size_t q1_qmm_workspace_bytes(int64_t M, const q1_weight* w) {
   }
   if (M == 0) return 0;
   if (M <= g_max_rows) {
-    q1::GemvPlan p;
+    PackedPlan p;
     const char* why = "";
-    if (!q1::plan_gemv((int)M, w->N, w->K, false, !w->symmetric, &p, &why)) {
+    if (!plan_packed((int)M, w->N, w->K, false, !w->symmetric, &p, &why)) {
       fail(Q1_ERR_UNSUPPORTED, "%s", why);
       return 0;
     }
@@ -258,9 +290,9 @@ q1_status q1_qmm(const void* x, int32_t x_dtype, int64_t M, const q1_weight* w, 
   const q1::QMat a = to_mat(w);
   auto* ws = static_cast<unsigned char*>(workspace);
   if (M <= g_max_rows) {
-    q1::GemvPlan p;
+    PackedPlan p;
     const char* why = "";
-    if (!q1::plan_gemv((int)M, w->N, w->K, false, !w->symmetric, &p, &why)) return fail(Q1_ERR_UNSUPPORTED, "%s", why);
+    if (!plan_packed((int)M, w->N, w->K, false, !w->symmetric, &p, &why)) return fail(Q1_ERR_UNSUPPORTED, "%s", why);
     return run_packed(p, static_cast<const uint16_t*>(x), w->K, a, nullptr, y, y_dtype, w->N, ws, kReserved, s);
   }
   uint16_t* deq = reinterpret_cast<uint16_t*>(ws + kReserved);

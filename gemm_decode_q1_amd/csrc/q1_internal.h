@@ -84,6 +84,53 @@ struct GemvArgs {
 template <int M>
 hipError_t launch_gemv_m(const GemvPlan& plan, const GemvArgs& args, bool affine, bool mbf16, hipStream_t stream);
 
+// ---- matrix-core packed path ------------------------------------------------
+
+// Plan of one matrix-core packed launch (see q1_mma.hip for the scheme).
+struct MmaPlan {
+  int M;
+  int pair;        // 1: FFN gate/up (two matrices, SiLU(g)*u epilogue)
+  int G;           // groups of 128 along K
+  int nspan;       // spans of 4 groups (512 weights)
+  int64_t ntiles;  // tiles of 16 rows
+  int S;           // K segments (grid split); S > 1 finishes in the kernel
+  int KSP;         // spans per K segment (the last may have fewer)
+  int NWS, NWT;    // waves splitting a segment's spans x waves splitting its tiles
+  int TB;          // (1)
+  int P;           // workgroups per K segment
+  int nb;          // tiles per wave
+  int cgroup;      // S > 1: tiles per arrival counter
+  int64_t wgs;     // S * P
+  size_t lds_bytes;
+  size_t partial_floats;  // S > 1: S*M*N*(pair ? 2 : 1)
+  size_t counters;        // S > 1: nb * P
+};
+
+struct MmaArgs {
+  const uint16_t* x;
+  int64_t x_ld;
+  const uint32_t* p0;
+  const uint32_t* p1;
+  const uint16_t* s0;
+  const uint16_t* s1;
+  const uint16_t* b0;
+  const uint16_t* b1;
+  int64_t N;
+  int32_t M, K, G, nspan;
+  int32_t S, KSP, NWS, NWT, P, nb, cgroup;
+  uint32_t x_bytes, packed_bytes, meta_bytes;
+  int32_t out_dtype;
+  void* out;
+  int64_t out_ld;
+  float* partial;
+  uint32_t* counters;
+};
+
+bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* plan, const char** why);
+
+hipError_t launch_mma(const MmaPlan& plan, const uint16_t* x, int64_t x_ld, const QMat& a, const QMat* b, void* out,
+                      int32_t out_dtype, int64_t out_ld, float* partial, uint32_t* counters, hipStream_t stream);
+
 // Returns false (with a message) when the request cannot be planned.
 bool plan_gemv(int M, int64_t N, int64_t K, bool pair, bool affine, GemvPlan* plan, const char** why);
 

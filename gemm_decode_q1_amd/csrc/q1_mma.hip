@@ -1,0 +1,683 @@
+// Packed narrow-M Q1 matmul on the CDNA4 matrix cores.
+//
+//   y[m][n] = sum_k x[m][k] * w[n][k],   w = s*bit + b   (symmetric: b = -s/2)
+//
+// for M <= 8 activation rows, straight from the packed weights (Higgs PR #212,
+// "What": narrow Q1 matmuls stay packed; rMLX issue #207 for the format: 32
+// weights per uint32, LSB first, one scale and bias per 128 weights).
+//
+// Per weight row n and group g of 128 weights
+//   sum_k w x = s*S + b*X,   S = sum_k bit_k x_k,   X = sum_k x_k
+// (symmetric: s*(S - X/2)).  S is the product of a 0/1 matrix with the
+// activations, and that product runs on v_mfma_scale_f32_16x16x128_f8f6f4:
+//
+// * B operand: the bits of one packed word per lane, expanded to fp4 (E2M1)
+//   codes with four bit-masks (no shifts):
+//     w & 0x11111111 -> nibble = bit 4i   -> code 0.5 * bit
+//     w & 0x22222222 -> nibble = bit 4i+1 -> code 1.0 * bit
+//     w & 0x44444444 -> nibble = bit 4i+2 -> code 2.0 * bit
+//     (w & 0x88888888) | 0x22222222 -> bit 4i+3 -> code 1 - 2*bit
+//   The matching activation (A operand) is scaled by 2, 1, 1/2, -1/2, so each
+//   product is bit*x, except the last class, which adds -x/2; the MFMA's
+//   accumulator input cancels that (and adds -X/2 for symmetric tensors).
+// * A operand: each activation as two fp8 (E4M3) pieces, x = hi + lo/16, with
+//   one power-of-two block scale per 32 weights chosen from the block's
+//   largest |x|.  A bf16 value has 8 significant bits, hi carries the top 4
+//   and lo the rest, so the pair is exact for every element within 2^14 of
+//   its block's largest magnitude; below that the error is at most 2^-21 of
+//   the block maximum.  Rows 0..7 of the 16-row A tile hold hi for the M
+//   activation rows and rows 8..15 hold lo; the two halves of the result are
+//   added at the end.
+// * One instruction covers 16 weight rows x one group (128 weights): its fp32
+//   result is multiplied by the group scale (and the bias term added) on the
+//   vector ALU.
+//
+// Operand layouts of the instruction (gfx950, fp8 A / fp4 B):
+//   A lane l: row l%16; byte e holds k-index 16*(l/16) + e (e < 16) or
+//             64 + 16*(l/16) + e - 16 (e >= 16); the scale of (row r, 32-k
+//             block j) is in lane r + 16*j, byte op_sel.
+//   B lane l: column l%16; code e (dword e/8, nibble e%8) holds k-index
+//             32*(l/16) + e, so lane l/16 = q carries word q of the group.
+//   D lane l: column l%16, rows 4*(l/16) .. +3.
+//
+// Work decomposition.  A workgroup (8 waves) owns a block of row tiles (16
+// rows each) and a segment of K (spans of 4 groups).  First every thread
+// converts the segment's activations into the A operand image in LDS; then
+// wave (ws, wt) takes spans ws, ws+NWS.. of the segment and tiles wt, wt+NWT..
+// of the block.  A lane loads 16 bytes = one group's 4 words of one row; a
+// 4x4 transpose across the lane quarters (two permlane32 and two permlane16
+// swaps) gives lane quarter q word q of each of the 4 groups.  The waves'
+// partial sums meet in LDS and are added in a fixed order.  With more than one
+// K segment (grid split), each segment writes fp32 partials with agent-scope
+// stores and the last workgroup to finish a row block adds them in segment
+// order, so results never depend on timing.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "q1_device.h"
+#include "q1_internal.h"
+
+namespace q1 {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kNW = 8;  // waves per workgroup
+constexpr int kThreads = kNW * 64;
+constexpr int kKspMax = 14;  // spans per K segment (LDS image 126 KB at most)
+
+// LDS image of one span (4 groups): A operand [g4][half][64 lanes][16 B],
+// block scales [64 lanes][4 groups] bytes, accumulator inputs and group sums
+// [g4][16 D rows] floats (rows 8..15, the lo half, and rows of activation
+// index >= M hold zeros; inactive A rows hold zero bytes and unit scales).
+constexpr int kSpanA = 8192;
+constexpr int kOffSc = kSpanA;
+constexpr int kOffCorr = kOffSc + 256;
+constexpr int kOffXs = kOffCorr + 256;
+constexpr int kSpanLds = kOffXs + 256;
+
+constexpr uint32_t kBufWord3 = 0x00020000u;
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kBufWord3);
+}
+
+__device__ __forceinline__ float dpp_xor1(float v) {  // quad_perm [1,0,3,2]
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {  // quad_perm [2,3,0,1]
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_half_mirror(float v) {  // lane i <- lane 7-i within 8
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xf, 0xf, false));
+}
+
+// Conversion of the activations of spans [span0, span0 + nsp) into the LDS
+// image.  Item = (row m, span, word, half word): 16 activations, one dword of
+// A bytes per bit class, for the hi and the lo piece.  The loads of all of a
+// thread's items (at most kPrepRounds) are issued first (prep_load), so they
+// can be in flight together with the weight loads issued right after them.
+constexpr int kPrepRounds = 8;
+
+struct PrepLoads {
+  u32x4 q[kPrepRounds][2];
+};
+
+__device__ __forceinline__ void prep_load(const MmaArgs& a, int span0, int nsp, int tid, PrepLoads& L) {
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, a.x_bytes);
+  const int items = a.M * nsp * 32;
+#pragma unroll
+  for (int r = 0; r < kPrepRounds; ++r) {
+    const int it = tid + r * kThreads;
+    const bool valid = it < items;
+    const int hh = it & 1, wi = (it >> 1) & 15, ms = it >> 5;
+    const int m = valid ? ms / nsp : 0;
+    const int sp = valid ? ms - m * nsp : 0;
+    const int k0 = (span0 + sp) * 512 + wi * 32 + hh * 16;
+    const uint32_t off = (uint32_t)(((int64_t)m * a.x_ld + k0) * 2) | ((valid && k0 < a.K) ? 0u : kOOB);
+    if (r * kThreads < items) {  // uniform: skip rounds nobody needs
+      L.q[r][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+      L.q[r][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0);
+    }
+  }
+}
+
+template <bool AFFINE>
+__device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int tid, const PrepLoads& L) {
+  // rows no item writes: inactive A rows, their scales, lo/inactive sums
+  for (int idx = tid; idx < nsp * 512; idx += kThreads) {  // 16-byte A chunks
+    const int mrow = idx & 15;
+    if ((mrow & 7) >= a.M) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4*>(lds + (idx >> 9) * kSpanLds)[idx & 511] = z;
+    }
+  }
+  for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // scale dwords, one per lane
+    if (((idx & 15) & 7) >= a.M) reinterpret_cast<uint32_t*>(lds + (idx >> 6) * kSpanLds + kOffSc)[idx & 63] = 0x7f7f7f7fu;
+  }
+  for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // [g4][16] sums
+    const int r = idx & 15;
+    if (r >= a.M) {
+      float* base = reinterpret_cast<float*>(lds + (idx >> 6) * kSpanLds);
+      base[kOffCorr / 4 + (idx & 63)] = 0.0f;
+      base[kOffXs / 4 + (idx & 63)] = 0.0f;
+    }
+  }
+  const int items = a.M * nsp * 32;
+#pragma unroll
+  for (int r = 0; r < kPrepRounds; ++r) {
+    if (r * kThreads >= items) break;  // uniform; rounds with items keep whole waves (items % 64 == 0)
+    const int it = tid + r * kThreads;
+    const bool valid = it < items;
+    const int hh = it & 1, wi = (it >> 1) & 15, ms = it >> 5;
+    const int m = valid ? ms / nsp : 0;
+    const int sp = valid ? ms - m * nsp : 0;
+    const int g4 = wi >> 2, b = wi & 3;
+    float xv[16];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t wd = d < 4 ? L.q[r][0][d] : L.q[r][1][d - 4];
+      xv[2 * d] = __uint_as_float(wd << 16);
+      xv[2 * d + 1] = __uint_as_float(wd & 0xffff0000u);
+    }
+    // element t has bit position 16*hh + t in the word: class t % 4
+    float cm[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      cm[j] = fmaxf(fmaxf(fabsf(xv[j]), fabsf(xv[j + 4])), fmaxf(fabsf(xv[j + 8]), fabsf(xv[j + 12])));
+    float amax = fmaxf(fmaxf(2.0f * cm[0], cm[1]), 0.5f * fmaxf(cm[2], cm[3]));
+    amax = fmaxf(amax, dpp_xor1(amax));  // the word's other half
+    int sc = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 8 : 0;
+    sc = sc < -123 ? -123 : (sc > 127 ? 127 : sc);
+    const float alpha[4] = {2.0f, 1.0f, 0.5f, -0.5f};
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float f = ldexpf(alpha[j], -sc);
+      const float v0 = xv[j] * f, v1 = xv[j + 4] * f, v2 = xv[j + 8] * f, v3 = xv[j + 12] * f;
+      int h = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+      h = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, h, true);
+      const float r0 = (v0 - __builtin_amdgcn_cvt_f32_fp8(h, 0)) * 16.0f;
+      const float r1 = (v1 - __builtin_amdgcn_cvt_f32_fp8(h, 1)) * 16.0f;
+      const float r2 = (v2 - __builtin_amdgcn_cvt_f32_fp8(h, 2)) * 16.0f;
+      const float r3 = (v3 - __builtin_amdgcn_cvt_f32_fp8(h, 3)) * 16.0f;
+      int l = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+      l = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, l, true);
+      hi[j] = (uint32_t)h;
+      lo[j] = (uint32_t)l;
+    }
+    float X = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) X += xv[t];
+    float X3 = (xv[3] + xv[7]) + (xv[11] + xv[15]);
+    // sums over the group's 8 items (4 words x 2 halves)
+    X += dpp_xor1(X);
+    X3 += dpp_xor1(X3);
+    X += dpp_xor2(X);
+    X3 += dpp_xor2(X3);
+    X += dpp_half_mirror(X);
+    X3 += dpp_half_mirror(X3);
+    if (valid) {
+      unsigned char* base = lds + sp * kSpanLds;
+      const int h2 = b >> 1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int qa = 2 * (b & 1) + (j >> 1);
+        const int dw = 2 * (j & 1) + hh;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(base + (g4 * 8 + h2 * 4 + qa) * 256 + m * 16 + dw * 4);
+        dst[0] = hi[j];
+        dst[32] = lo[j];  // row 8 + m: 8 rows * 16 B further
+      }
+      if (hh == 0) {
+        base[kOffSc + (m + 16 * b) * 4 + g4] = (unsigned char)(sc + 127);
+        base[kOffSc + (8 + m + 16 * b) * 4 + g4] = (unsigned char)(sc + 123);
+      }
+      if ((it & 7) == 0) {
+        reinterpret_cast<float*>(base + kOffCorr)[g4 * 16 + m] = AFFINE ? 0.5f * X3 : 0.5f * (X3 - X);
+        reinterpret_cast<float*>(base + kOffXs)[g4 * 16 + m] = X;
+      }
+    }
+  }
+}
+
+template <bool MBF16>
+__device__ __forceinline__ float meta_f32(uint32_t bits) {
+  return MBF16 ? __uint_as_float(bits << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
+// (lgkmcnt 0), not for its global loads, so the load ring stays in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+}
+
+// 4x4 transpose of (lane quarter, component): afterwards quarter q holds, in
+// component c, what quarter c held in component q.
+__device__ __forceinline__ void transpose_quarters(u32x4& w) {
+  auto r02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+  auto r13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+  auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
+  auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
+  w[0] = r01[0];
+  w[1] = r01[1];
+  w[2] = r23[0];
+  w[3] = r23[1];
+}
+
+// Scales (or biases) of one row for the 4 groups of a span, one register each.
+// Groups past the end read 0.
+// (Each value stays in its own register until use: combining two 16-bit
+// loads right after issue would make the wave wait for them.)
+// With G % 4 == 0 the 4 values are one aligned 8-byte load (two registers of
+// packed 16-bit values); otherwise 4 loads of 16 bits, one register each.
+template <bool SC64>
+__device__ __forceinline__ void load_meta4(__amdgpu_buffer_rsrc_t r, bool rowok, uint32_t row_off, int G, int g0,
+                                           uint32_t* v) {
+  if (SC64) {
+    const uint32_t o = (row_off + (uint32_t)g0 * 2) | (rowok ? 0u : kOOB);
+    const auto d = __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0);
+    v[0] = d[0];
+    v[1] = d[1];
+  } else {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t o = (row_off + (uint32_t)(g0 + g) * 2) | ((rowok && g0 + g < G) ? 0u : kOOB);
+      v[g] = __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, 0);
+    }
+  }
+}
+
+template <bool MBF16, bool SC64>
+__device__ __forceinline__ float meta_at(const uint32_t* v, int g) {
+  if (SC64) return meta_f32<MBF16>((g & 1) ? (v[g >> 1] >> 16) : (v[g >> 1] & 0xffffu));
+  return meta_f32<MBF16>(v[g]);
+}
+
+// Work of a wave: tiles k = 0, 1, .. of its column (tile ((k*P + p)*NWT + wt):
+// consecutive tiles of a wave are P*NWT tiles apart, so the last round
+// spreads evenly), and for each tile the spans [sp_lo, sp_hi) of its slice of
+// the segment, spans inner: a tile's 16 rows are contiguous in memory, so the
+// loads in flight cover a compact block.  Item i = (tile k, span s) sits in
+// ring slot i % D; its loads are issued D items ahead.
+template <bool AFFINE, bool MBF16, bool PAIR, bool SC64>
+__global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
+  constexpr int NMAT = PAIR ? 2 : 1;
+  constexpr int D = 8;
+  extern __shared__ __align__(16) unsigned char lds[];
+  __shared__ int last_flag;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int seg = (int)(blockIdx.x % (unsigned)a.S);
+  const int p = (int)(blockIdx.x / (unsigned)a.S);
+  const int span0 = seg * a.KSP;
+  const int nsp = (span0 + a.KSP <= a.nspan) ? a.KSP : a.nspan - span0;
+  const int ws = wave % a.NWS, wt = wave / a.NWS;
+  const int sp_lo = (ws * nsp) / a.NWS, sp_hi = ((ws + 1) * nsp) / a.NWS;
+  const int nspw = sp_hi - sp_lo;  // >= 1: the plan keeps NWS <= spans of every segment
+  const int nitems = a.nb * nspw;  // a.nb = tiles per wave
+  float* red = reinterpret_cast<float*>(lds + (size_t)a.KSP * kSpanLds);
+
+  const __amdgpu_buffer_rsrc_t rp[2] = {rsrc(a.p0, a.packed_bytes), rsrc(PAIR ? a.p1 : a.p0, a.packed_bytes)};
+  const __amdgpu_buffer_rsrc_t rs[2] = {rsrc(a.s0, a.meta_bytes), rsrc(PAIR ? a.s1 : a.s0, a.meta_bytes)};
+  const __amdgpu_buffer_rsrc_t rbias[2] = {rsrc(AFFINE ? a.b0 : a.s0, a.meta_bytes),
+                                           rsrc(AFFINE && PAIR ? a.b1 : a.s0, a.meta_bytes)};
+
+  const int nl = lane & 15;  // weight row within a tile (B and D column)
+  const int q = lane >> 4;   // lane quarter
+  const uint32_t row_bytes = (uint32_t)a.K >> 3;
+  const uint32_t q16 = (uint32_t)q * 16u;
+  // row indices fit in 31 bits (the plan keeps N*K/8 below 2^31)
+  const int Nrows = (int)a.N;
+  auto tile_of = [&](int k) -> int { return (k * a.P + p) * a.NWT + wt; };
+
+  u32x4 words[D][NMAT];
+  uint32_t sreg[D][NMAT][4];
+  uint32_t breg[D][NMAT][4];
+  float acc[NMAT][4];
+#pragma unroll
+  for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0f;
+
+  // issue the loads of item (tile k, span s) into slot u
+  auto issue = [&](int u, int k, int sidx, bool ok) {
+    const int span = span0 + sp_lo + sidx;
+    const int n = tile_of(k) * 16 + nl;
+    const bool rowok = ok && n < Nrows;
+    // out-of-range lanes get bit 31 set (past every buffer): no branches
+    const uint32_t wo = ((uint32_t)n * row_bytes + (uint32_t)(span * 64) + q16) |
+                        ((rowok && 4 * span + q < a.G) ? 0u : kOOB);
+    const uint32_t mo = (uint32_t)n * (uint32_t)a.G * 2u;
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+      words[u][mt] = __builtin_amdgcn_raw_buffer_load_b128(rp[mt], wo, 0, 2);
+      load_meta4<SC64>(rs[mt], rowok, mo, a.G, 4 * span, sreg[u][mt]);
+      if (AFFINE) load_meta4<SC64>(rbias[mt], rowok, mo, a.G, 4 * span, breg[u][mt]);
+    }
+  };
+
+  // activation loads first, then the first D items of weights, then the
+  // conversion (which waits for the activations only)
+  PrepLoads pl;
+  prep_load(a, span0, nsp, tid, pl);
+  {
+    int k = 0, sidx = 0;
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      issue(u, k, sidx, u < nitems);
+      if (++sidx == nspw) {
+        sidx = 0;
+        ++k;
+      }
+    }
+  }
+  prep_compute<AFFINE>(a, nsp, lds, tid, pl);
+  lds_barrier();
+
+  // A rows: lane's row m' = lane % 16 carries activation row m' % 8 (hi for
+  // m' < 8, lo for m' >= 8); only rows of activation index < M are read.
+  const bool arow = (nl & 7) < a.M;
+
+  auto compute = [&](int u, int spl) {
+    const unsigned char* base = lds + (sp_lo + spl) * kSpanLds;
+    const uint32_t scale_a = reinterpret_cast<const uint32_t*>(base + kOffSc)[lane];
+    v8i A[4];
+    v4f C[4], XS[4];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      u32x4 h0 = {0u, 0u, 0u, 0u}, h1 = {0u, 0u, 0u, 0u};
+      if (arow) {
+        h0 = reinterpret_cast<const u32x4*>(base + (g4 * 8) * 256)[lane];
+        h1 = reinterpret_cast<const u32x4*>(base + (g4 * 8 + 4) * 256)[lane];
+      }
+      A[g4] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+      C[g4] = reinterpret_cast<const v4f*>(base + kOffCorr)[g4 * 4 + q];
+      if (AFFINE) XS[g4] = reinterpret_cast<const v4f*>(base + kOffXs)[g4 * 4 + q];
+    }
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+      u32x4 w = words[u][mt];
+      transpose_quarters(w);
+      v4f Dg[4];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const uint32_t wd = w[g4];
+        const v8i B = {(int)(wd & 0x11111111u), (int)(wd & 0x22222222u), (int)(wd & 0x44444444u),
+                       (int)((wd & 0x88888888u) | 0x22222222u), 0, 0, 0, 0};
+        if (g4 == 0)
+          Dg[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, C[0], 0, 4, 0, (int)scale_a, 0, 0x7f7f7f7f);
+        else if (g4 == 1)
+          Dg[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, C[1], 0, 4, 1, (int)scale_a, 0, 0x7f7f7f7f);
+        else if (g4 == 2)
+          Dg[2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, C[2], 0, 4, 2, (int)scale_a, 0, 0x7f7f7f7f);
+        else
+          Dg[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[3], B, C[3], 0, 4, 3, (int)scale_a, 0, 0x7f7f7f7f);
+      }
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float sv = meta_at<MBF16, SC64>(sreg[u][mt], g4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(sv, Dg[g4][i], acc[mt][i]);
+        if (AFFINE) {
+          const float bv = meta_at<MBF16, SC64>(breg[u][mt], g4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(bv, XS[g4][i], acc[mt][i]);
+        }
+      }
+    }
+  };
+
+  auto final_store = [&](int m, int row, const float* v) {
+    if (PAIR)
+      static_cast<uint16_t*>(a.out)[m * a.out_ld + row] = (uint16_t)f32_to_bf16_bits(silu_f32(v[0]) * v[1]);
+    else
+      store_out(a.out, a.out_dtype, m * a.out_ld + row, v[0]);
+  };
+
+  // After tile k: lane l of half ab holds activation row
+  // 4*((l>>4)&1) + 2*ab + (l>>5) of weight row l & 15 (hi + lo combined).
+  // A wave that owns whole tiles stores them; otherwise the result waits in
+  // LDS (red[ws][wt][k][mt][ab][64]) for the reduction after the loop.
+  auto tile_done = [&](int k) {
+    float comb[NMAT][2];
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+      auto p01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[mt][0]), __float_as_uint(acc[mt][1]), false,
+                                                  false);
+      auto p23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[mt][2]), __float_as_uint(acc[mt][3]), false,
+                                                  false);
+      comb[mt][0] = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
+      comb[mt][1] = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0f;
+    }
+    if (a.NWS == 1) {  // (the plan uses one K segment here)
+      const int row = tile_of(k) * 16 + nl;
+      const int mA = 4 * ((lane >> 4) & 1) + (lane >> 5);
+      if (row < Nrows) {
+#pragma unroll
+        for (int ab = 0; ab < 2; ++ab) {
+          const int m = mA + 2 * ab;
+          if (m < a.M) {
+            float v[NMAT];
+#pragma unroll
+            for (int mt = 0; mt < NMAT; ++mt) v[mt] = comb[mt][ab];
+            final_store(m, row, v);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+        for (int ab = 0; ab < 2; ++ab)
+          red[((((ws * a.NWT + wt) * a.nb + k) * NMAT + mt) * 2 + ab) * 64 + lane] = comb[mt][ab];
+    }
+  };
+
+  // Whole turns of the ring (items past the end load nothing and add zeros;
+  // their tile index is >= nb, so they emit nothing): a loop body without
+  // early exits keeps the ring in place across iterations.
+  const int nitems_pad = (nitems + D - 1) / D * D;
+  int k = 0, sidx = 0;    // current item
+  int ik = 0, isidx = 0;  // item + D (next loads)
+  isidx = D;
+  while (isidx >= nspw) {
+    isidx -= nspw;
+    ++ik;
+  }
+  for (int base = 0; base < nitems_pad; base += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      compute(u, sidx);
+      issue(u, ik, isidx, base + u + D < nitems);
+      __builtin_amdgcn_sched_barrier(0);  // keep items apart: bounded register use
+      if (sidx == nspw - 1 && k < a.nb) tile_done(k);
+      if (++sidx == nspw) {
+        sidx = 0;
+        ++k;
+      }
+      if (++isidx == nspw) {
+        isidx = 0;
+        ++ik;
+      }
+    }
+  }
+  if (a.NWS == 1) return;
+
+  // ---- the waves of the segment's spans meet: sum over ws in order ----
+  lds_barrier();
+  const int nout = a.NWT * a.nb * 128;
+  for (int o = tid; o < nout; o += kThreads) {
+    const int wt2 = o / (a.nb * 128), rem = o - wt2 * (a.nb * 128);
+    const int k2 = rem >> 7, r = rem & 127, ab = r >> 6, l = r & 63;
+    const int m = 4 * ((l >> 4) & 1) + 2 * ab + (l >> 5);
+    const int row = ((k2 * a.P + p) * a.NWT + wt2) * 16 + (l & 15);
+    if (m >= a.M || row >= Nrows) continue;
+    float v[NMAT];
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+      float sum = 0.0f;
+      for (int w2 = 0; w2 < a.NWS; ++w2) sum += red[((((w2 * a.NWT + wt2) * a.nb + k2) * NMAT + mt) * 2 + ab) * 64 + l];
+      v[mt] = sum;
+    }
+    if (a.S == 1) {
+      final_store(m, row, v);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt)
+        __hip_atomic_store(&a.partial[(((int64_t)seg * a.M + m) * NMAT + mt) * a.N + row], v[mt], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (a.S == 1) return;
+
+  // ---- split K (NWT == 1): the last of the S workgroups with this p adds
+  // the partials of p's tiles in segment order ----
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are performed
+  lds_barrier();
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&a.counters[p], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = old == (uint32_t)(a.S - 1);
+  }
+  lds_barrier();
+  if (!last_flag) return;
+  const int nfin = a.nb * 16 * a.M;
+  for (int o = tid; o < nfin; o += kThreads) {
+    const int m = o / (a.nb * 16), rem = o - m * (a.nb * 16);
+    const int k2 = rem >> 4;
+    const int row = (k2 * a.P + p) * 16 + (rem & 15);
+    if (row >= Nrows) continue;
+    float v[NMAT];
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+      float sum = 0.0f;
+      for (int s2 = 0; s2 < a.S; ++s2)
+        sum += __hip_atomic_load(&a.partial[(((int64_t)s2 * a.M + m) * NMAT + mt) * a.N + row], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      v[mt] = sum;
+    }
+    final_store(m, row, v);
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[p], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+template <bool AFFINE, bool MBF16, bool PAIR, bool SC64>
+hipError_t launch_k(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&q1_mma_kernel<AFFINE, MBF16, PAIR, SC64>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 64);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((q1_mma_kernel<AFFINE, MBF16, PAIR, SC64>), dim3((unsigned)p.wgs), dim3(kThreads), p.lds_bytes,
+                     s, a);
+  return hipGetLastError();
+}
+
+template <bool AFFINE, bool MBF16, bool PAIR>
+hipError_t launch_t(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
+  return (a.G % 4 == 0) ? launch_k<AFFINE, MBF16, PAIR, true>(p, a, s) : launch_k<AFFINE, MBF16, PAIR, false>(p, a, s);
+}
+
+}  // namespace
+
+bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, const char** why) {
+  (void)affine;
+  if (M < 1 || M > 8) {
+    *why = "matrix-core packed path handles 1..8 activation rows";
+    return false;
+  }
+  if (N < 1 || K < 128 || K % 128 != 0) {
+    *why = "bad shape";
+    return false;
+  }
+  if (N * (K / 8) >= ((int64_t)1 << 31) || N * (K / 128) * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)M * K * 2 >= ((int64_t)1 << 31)) {
+    *why = "matrix too large for 32-bit buffer offsets (split it along N)";
+    return false;
+  }
+  const int nmat = pair ? 2 : 1;
+  const int cus = device_cus();
+  p->M = M;
+  p->pair = pair ? 1 : 0;
+  p->G = (int)(K / 128);
+  p->nspan = (p->G + 3) / 4;
+  p->ntiles = (N + 15) / 16;
+  p->S = (p->nspan + kKspMax - 1) / kKspMax;
+  p->KSP = (p->nspan + p->S - 1) / p->S;
+  p->S = (p->nspan + p->KSP - 1) / p->KSP;
+  const int last_seg = p->nspan - (p->S - 1) * p->KSP;  // spans of the shortest segment
+  // With few tiles per CU (or a split K) the waves of a workgroup share its
+  // tiles and split the segment's spans; otherwise each wave owns whole tiles.
+  const int64_t tiles_per_cu = (p->ntiles * p->S + cus - 1) / cus;
+  int nws = 1;
+  if (p->S > 1 || tiles_per_cu < 2 * kNW)
+    while (nws * 2 <= kNW && nws * 2 <= last_seg) nws *= 2;
+  if (p->S > 1 && nws != kNW) {
+    *why = "split K needs at least 8 spans per segment";
+    return false;
+  }
+  p->NWS = nws;
+  p->NWT = kNW / nws;
+  p->TB = 1;
+  int64_t P = (p->ntiles + p->NWT - 1) / p->NWT;
+  const int64_t cap = cus / p->S > 0 ? cus / p->S : 1;
+  if (P > cap) P = cap;
+  p->P = (int)P;
+  p->nb = (int)((p->ntiles + P * p->NWT - 1) / (P * p->NWT));  // tiles per wave
+  p->wgs = (int64_t)p->S * P;
+  p->lds_bytes = (size_t)p->KSP * kSpanLds + (nws > 1 ? (size_t)kNW * p->nb * nmat * 512 : 0);
+  if ((int64_t)M * p->KSP * 32 > (int64_t)kPrepRounds * kThreads) {
+    *why = "activation conversion exceeds its register rounds";
+    return false;
+  }
+  if (p->lds_bytes > 160 * 1024 - 64) {
+    *why = "LDS budget exceeded";
+    return false;
+  }
+  p->cgroup = 1;
+  p->partial_floats = p->S > 1 ? (size_t)p->S * M * N * nmat : 0;
+  p->counters = p->S > 1 ? (size_t)P : 0;  // one per workgroup column p (P <= CUs)
+  return true;
+}
+
+hipError_t launch_mma(const MmaPlan& p, const uint16_t* x, int64_t x_ld, const QMat& a, const QMat* b, void* out,
+                      int32_t out_dtype, int64_t out_ld, float* partial, uint32_t* counters, hipStream_t s) {
+  MmaArgs g;
+  g.x = x;
+  g.x_ld = x_ld;
+  g.p0 = a.packed;
+  g.s0 = a.scales;
+  g.b0 = a.biases;
+  g.p1 = b ? b->packed : a.packed;
+  g.s1 = b ? b->scales : a.scales;
+  g.b1 = b ? b->biases : a.biases;
+  g.N = a.N;
+  g.M = p.M;
+  g.K = (int32_t)a.K;
+  g.G = p.G;
+  g.nspan = p.nspan;
+  g.S = p.S;
+  g.KSP = p.KSP;
+  g.NWS = p.NWS;
+  g.NWT = p.NWT;
+  g.P = p.P;
+  g.nb = p.nb;
+  g.cgroup = p.cgroup;
+  g.x_bytes = (uint32_t)(((p.M - 1) * x_ld + a.K) * 2);
+  g.packed_bytes = (uint32_t)(a.N * (a.K / 8));
+  g.meta_bytes = (uint32_t)(a.N * (a.K / 128) * 2);
+  g.out_dtype = out_dtype;
+  g.out = out;
+  g.out_ld = out_ld;
+  g.partial = partial;
+  g.counters = counters;
+  const bool affine = !a.symmetric, mbf16 = a.meta_bf16 != 0, pair = b != nullptr;
+  if (pair) {
+    if (affine) return mbf16 ? launch_t<true, true, true>(p, g, s) : launch_t<true, false, true>(p, g, s);
+    return mbf16 ? launch_t<false, true, true>(p, g, s) : launch_t<false, false, true>(p, g, s);
+  }
+  if (affine) return mbf16 ? launch_t<true, true, false>(p, g, s) : launch_t<true, false, false>(p, g, s);
+  return mbf16 ? launch_t<false, true, false>(p, g, s) : launch_t<false, false, false>(p, g, s);
+}
+
+}  // namespace q1
