@@ -8,16 +8,24 @@ must read) for the whole step.  Each launch reads a different copy of the
 weights, rotating through more copies than the 256 MB last-level cache holds,
 so reads come from HBM.
 
+``roofline`` covers the dominant kernel of the step (the matrix-core kernel,
+M = 2..8): its average launch duration comes from HIP events around runs of
+back-to-back launches on the launch stream (so it includes the short dispatch
+gap between kernels), and its HBM traffic from the committed rocprofv3 counter
+summary when that summary was taken from the current kernel sources.
+
 The same run also measures, once each, the other rows of the path (tied LM head
 M=1, down projection, embedding gather, dequantisation, the wide M=512 fallback
 and the fused FFN) and times the CPU oracle on a bounded sample of the headline
 workload.  Prints one JSON line.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
 import platform
+import re
 import sys
 import time
 
@@ -28,6 +36,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "Q1 GEMV effective HBM GB/s (% of 8 TB/s) at M=1..8; GEMM TFLOP/s at M=512"
 ROTATE_BYTES = 1 << 30  # rotate weight copies over at least 1 GiB (> 256 MB MALL + L2)
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "q1_mma_kernel_ffn_up_K5120_N17408_M2to8_pmc.txt")
+DOMINANT = "q1_mma_kernel"
+DOMINANT_MS = list(range(2, 9))
 
 
 def parse():
@@ -37,7 +48,35 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--quick", action="store_true", help="headline step only (for profiling)")
+    p.add_argument("--copy-calib", action="store_true",
+                   help="also run a plain 256 MiB device copy (reference for the HBM byte counters)")
     return p.parse_args()
+
+
+def source_sha256() -> str:
+    """Hash of the kernel sources (identifies which build a counter profile belongs to)."""
+    d = os.path.join(ROOT, "gemm_decode_q1_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".inc", ".h", ".cpp")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when it is missing or was taken from other sources."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    m_sha = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_sha or not m_b or m_sha.group(1) != source_sha256():
+        return None
+    return float(m_b.group(1))
 
 
 def main():
@@ -72,23 +111,43 @@ def main():
                                   None if base.biases is None else base.biases.clone(), base.N, base.K))
         return out
 
-    class EventTimer:
-        """Per-launch durations from HIP events recorded on the launch stream."""
-
-        def __init__(self, n):
-            self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-            self.i = 0
-
-        def run(self, fn):
-            a, b = self.ev[self.i]
-            a.record(stream)
+    def capture(fns):
+        """A HIP graph of the launches in `fns` (after one eager run of each)."""
+        for fn in fns:
             fn()
-            b.record(stream)
-            self.i += 1
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for fn in fns:
+                fn()
+        return g
 
-        def times_ms(self):
-            torch.cuda.synchronize()
-            return [a.elapsed_time(b) for a, b in self.ev[:self.i]]
+    def replay_us(g, nlaunch, reps):
+        """Mean microseconds per launch over `reps` back-to-back replays of g,
+        from two HIP events on the stream the replays run on."""
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * nlaunch)
+
+    def run_batch(fns, reps):
+        """Mean microseconds per launch of `fns`, launched back to back from a
+        graph replay (the host's per-call cost does not enter)."""
+        return replay_us(capture(fns), len(fns), reps)
+
+    def ws_for(M, W):
+        n = Q.q1_qmm_workspace_bytes(M, W)
+        return torch.zeros(max(n, 256), dtype=torch.uint8, device="cuda") if n else None
+
+    def bw(nbytes, us):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"us": round(us, 2), "GB/s": round(gbs, 1), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1)}
 
     # ------------------------------------------------------------------ headline step
     wl2 = S.workload(2)
@@ -96,62 +155,58 @@ def main():
     bytes2 = w2.metric_bytes
     W2 = copies(w2, bytes2)
     x2 = xdev(wl2.x["x"])
-    y2 = torch.empty(8, w2.N, dtype=torch.bfloat16, device="cuda")
     Ms = list(range(1, 9))
-    rot = [0]
 
-    def step(timer=None):
-        for M in Ms:
-            W = W2[rot[0] % len(W2)]
-            rot[0] += 1
-            fn = lambda: Q.q1_qmm(x2[:M], W, y=y2[:M])
-            if timer is None:
-                fn()
-            else:
-                timer.run(fn)
+    ws2 = {M: ws_for(M, W2[0]) for M in Ms}
+    ys = [torch.empty(M, w2.N, dtype=torch.bfloat16, device="cuda") for M in Ms]
 
-    for _ in range(args.warmup):
-        step()
+    # One step = the eight launches; consecutive steps take the next copies of
+    # the weights.  The timed steps run as replays of a graph that holds
+    # `steps` steps (captured once), checked against an eager run first.
+    def step_fns(first_copy):
+        return [(lambda M=M, W=W2[(first_copy + i) % len(W2)]: Q.q1_qmm(x2[:M], W, y=ys[M - 1],
+                                                                          workspace=ws2[M]))
+                for i, M in enumerate(Ms)]
+
+    fns = [fn for s_ in range(args.steps) for fn in step_fns(s_ * len(Ms))]
+    for fn in fns[-len(Ms):]:
+        fn()
     torch.cuda.synchronize()
-    timer = EventTimer(args.steps * len(Ms))
+    eager = [y.clone() for y in ys]
+    g_step = capture(fns)
+    for _ in range(max(1, args.warmup)):
+        g_step.replay()
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, b) for a, b in zip(eager, ys)):
+        raise SystemExit("graph replay of the step differs from the eager result")
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record(stream)
-    for _ in range(args.steps):
-        step(timer)
+    g_step.replay()
     t1.record(stream)
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    per_launch = np.array(timer.times_ms()).reshape(args.steps, len(Ms))
-    ms_per_step = total_ms / args.steps
+    ms_per_step = t0.elapsed_time(t1) / args.steps
     value = len(Ms) * bytes2 / (ms_per_step * 1e-3) / 1e9
-    kern_us = per_launch.mean(axis=0) * 1e3
-    avg_launch_us = float(per_launch.mean() * 1e3)
-    achieved = bytes2 / (avg_launch_us * 1e-6) / 1e9
-    per_m = {str(M): {"us": round(float(kern_us[i]), 2), "GB/s": round(bytes2 / (kern_us[i] * 1e-6) / 1e9, 1),
-                      "pct_hbm": round(100 * bytes2 / (kern_us[i] * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
-             for i, M in enumerate(Ms)}
+    del g_step
 
-    detail = {"ffn_up_5120x17408_sym_f16_per_M": per_m}
+    # per-M launch durations (back-to-back launches over the rotating copies)
+    per_m = {}
+    for M in Ms:
+        us = run_batch([(lambda W=W, M=M: Q.q1_qmm(x2[:M], W, y=ys[M - 1], workspace=ws2[M])) for W in W2], 3)
+        per_m[str(M)] = bw(bytes2, us)
+    dom_us = float(np.mean([per_m[str(M)]["us"] for M in DOMINANT_MS]))
+    achieved = bytes2 / (dom_us * 1e-6) / 1e9
+    traffic = read_traffic()
+    detail = {"ffn_up_5120x17408_sym_f16_per_M": per_m,
+              "kernels": {"M=1": "q1_gemv_kernel (nibble tables)", "M=2..8": "q1_mma_kernel (fp8 x fp4 MFMA)"}}
 
-    def measure(fn_list, iters, bytes_per, flops_per=None):
-        """Mean per-launch microseconds over `iters` rounds of fn_list."""
-        for fn in fn_list[:2]:
-            fn()
-        tm = EventTimer(iters * len(fn_list))
-        for it in range(iters):
-            for fn in fn_list:
-                tm.run(fn)
-        t = np.array(tm.times_ms()).mean() * 1e3
-        r = {"us": round(float(t), 2)}
-        if bytes_per:
-            r["GB/s"] = round(bytes_per / (t * 1e-6) / 1e9, 1)
-            r["pct_hbm"] = round(100 * r["GB/s"] / HBM_PEAK_GBS, 1)
-        if flops_per:
-            r["TFLOP/s"] = round(flops_per / (t * 1e-6) / 1e12, 1)
-            r["pct_bf16_mfma"] = round(100 * r["TFLOP/s"] / BF16_PEAK_TFLOPS, 1)
-        return r
+    if args.copy_calib:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if not args.quick:
         # tied LM head, M=1, fp32 logits
@@ -160,13 +215,14 @@ def main():
         W4 = copies(w4, w4.metric_bytes)
         x4 = xdev(wl4.x["x"])
         y4 = torch.empty(1, w4.N, dtype=torch.float32, device="cuda")
-        detail["lm_head_5120x152064_M1"] = measure([(lambda W=W: Q.q1_qmm(x4, W, y=y4)) for W in W4], 4,
-                                                   w4.metric_bytes)
+        ws4 = ws_for(1, W4[0])
+        detail["lm_head_5120x152064_M1"] = bw(w4.metric_bytes, run_batch(
+            [(lambda W=W: Q.q1_qmm(x4, W, y=y4, workspace=ws4)) for W in W4], 3))
         # embedding gather of 4096 ids -> bf16 rows (read packed rows + scales, write bf16)
         ids = torch.from_numpy(wl4.ids).cuda()
         emb = torch.empty(4096, w4.K, dtype=torch.bfloat16, device="cuda")
         g_bytes = 4096 * (w4.K // 8 + w4.K // 128 * 2) + 4096 * w4.K * 2
-        detail["embed_gather_4096_rows"] = measure([lambda: Q.q1_embed_rows(ids, W4[0], out=emb)], 20, g_bytes)
+        detail["embed_gather_4096_rows"] = bw(g_bytes, run_batch([lambda: Q.q1_embed_rows(ids, W4[0], out=emb)], 20))
         del W4, emb
         # down projection, affine bf16, M=1..8
         wl3 = S.workload(3)
@@ -174,11 +230,11 @@ def main():
         W3 = copies(w3, w3.metric_bytes)
         x3 = xdev(wl3.x["x"])
         y3 = torch.empty(9, w3.N, dtype=torch.bfloat16, device="cuda")
-        d3 = {}
-        for M in Ms:
-            d3[str(M)] = measure([(lambda W=W, M=M: Q.q1_qmm(x3[:M], W, y=y3[:M])) for W in W3], 1,
-                                 w3.metric_bytes)
-        detail["ffn_down_17408x5120_affine_bf16_per_M"] = d3
+        ws3 = {M: ws_for(M, W3[0]) for M in Ms}
+        detail["ffn_down_17408x5120_affine_bf16_per_M"] = {
+            str(M): bw(w3.metric_bytes, run_batch(
+                [(lambda W=W, M=M: Q.q1_qmm(x3[:M], W, y=y3[:M], workspace=ws3[M])) for W in W3], 2))
+            for M in Ms}
         del W3
         # wide fallback at M=512: dequant to bf16 + MFMA GEMM (config 5a)
         wl5 = S.workload(5)
@@ -187,10 +243,14 @@ def main():
         x5 = xdev(wl5.x["x"])
         deq = torch.empty(g5.N, g5.K, dtype=torch.bfloat16, device="cuda")
         deq_bytes = g5.metric_bytes + g5.N * g5.K * 2
-        detail["dequant_17408x5120_to_bf16"] = measure([lambda: Q.q1_dequantize(G5, out=deq)], 10, deq_bytes)
+        detail["dequant_17408x5120_to_bf16"] = bw(deq_bytes, run_batch([lambda: Q.q1_dequantize(G5, out=deq)], 10))
         y5 = torch.empty(512, g5.N, dtype=torch.bfloat16, device="cuda")
         flops = 2.0 * 512 * g5.N * g5.K
-        detail["wide_M512_dequant_plus_gemm"] = measure([lambda: Q.q1_qmm(x5, G5, y=y5)], 10, None, flops)
+        ws5 = ws_for(512, G5)
+        us = run_batch([lambda: Q.q1_qmm(x5, G5, y=y5, workspace=ws5)], 10)
+        detail["wide_M512_dequant_plus_gemm"] = {"us": round(us, 2), "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 1),
+                                                 "pct_bf16_mfma": round(100 * flops / (us * 1e-6) / 1e12 /
+                                                                        BF16_PEAK_TFLOPS, 1)}
         # fused FFN, M=1..8 (three matrices, all symmetric fp16)
         FF = [Q.PackedQ1.from_host(wl5.weights[k]) for k in ("gate", "up", "down")]
         ffn_bytes = sum(wl5.weights[k].metric_bytes for k in ("gate", "up", "down"))
@@ -198,10 +258,12 @@ def main():
         FFc = [FF] + [[Q.PackedQ1(t.packed.clone(), t.scales.clone(), None, t.N, t.K) for t in FF]
                       for _ in range(reps - 1)]
         yf = torch.empty(8, 5120, dtype=torch.bfloat16, device="cuda")
-        df = {}
-        for M in Ms:
-            df[str(M)] = measure([(lambda F=F, M=M: Q.q1_ffn(x5[:M], *F, y=yf[:M])) for F in FFc], 2, ffn_bytes)
-        detail["fused_ffn_5120_17408_per_M"] = df
+        wsf = {M: torch.zeros(max(Q.q1_ffn_workspace_bytes(M, *FF), 256), dtype=torch.uint8, device="cuda")
+               for M in Ms}
+        detail["fused_ffn_5120_17408_per_M"] = {
+            str(M): bw(ffn_bytes, run_batch(
+                [(lambda F=F, M=M: Q.q1_ffn(x5[:M], *F, y=yf[:M], workspace=wsf[M])) for F in FFc], 2))
+            for M in Ms}
         torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ CPU oracle baseline
@@ -209,15 +271,22 @@ def main():
     if not args.no_cpu_baseline:
         import oracle as O
         cores = len(os.sched_getaffinity(0))
-        rows = np.arange(0, w2.N, 4)  # every 4th output row of the headline matrix
-        sample_bytes = rows.size * (w2.K // 8 + w2.K // 128 * 2)
+        # whole-matrix calls at M = 1, 2, .., 8, 1, .. until 10 s of CPU work
+        # have passed (one call takes a few seconds)
         t = time.perf_counter()
-        for M in Ms:
-            O.qmm_ref(wl2.x["x"][:M], w2.packed, w2.scales, None, w2.meta, True, w2.K, row_index=rows)
-        dt = time.perf_counter() - t
-        cpu = {"value": round(len(Ms) * sample_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-               "sample": f"oracle qmm_ref (fp32 dequant + fp64 matmul) on every 4th row ({rows.size} of {w2.N}) of "
-                         f"the K=5120 N=17408 matrix for M=1..8; {dt:.1f} s on {platform.processor() or 'host'}",
+        calls = []
+        while True:
+            M = Ms[len(calls) % len(Ms)]
+            O.qmm_ref(wl2.x["x"][:M], w2.packed, w2.scales, None, w2.meta, True, w2.K)
+            calls.append(M)
+            dt = time.perf_counter() - t
+            if dt >= 10.0:
+                break
+        cpu = {"value": round(len(calls) * bytes2 / dt / 1e9, 3), "unit": "GB/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"oracle qmm_ref (fp32 dequant + fp64 matmul) over the whole K=5120 N=17408 matrix, "
+                         f"{len(calls)} calls at M={','.join(map(str, calls))}, {dt:.1f} s on "
+                         f"{platform.processor() or 'host'}",
                "seconds": round(dt, 2)}
 
     out = {
@@ -236,10 +305,10 @@ def main():
         "config": {"workload": "ffn_up_projection_K5120_N17408_sym_f16_M1to8", "K": 5120, "N": 17408,
                    "M": "1..8", "group_size": 128, "metadata": "fp16 symmetric", "x": "bf16", "y": "bf16",
                    "bytes_per_launch": bytes2},
-        "roofline": {"bound": "hbm", "kernel": "q1_gemv_kernel", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(avg_launch_us, 2),
-                     "bytes_per_launch": bytes2},
+        "roofline": {"bound": "hbm", "kernel": DOMINANT, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "avg_launch_us": round(dom_us, 2), "launches": "M=2..8", "bytes_per_launch": bytes2},
         "cpu_baseline": cpu,
         "detail": detail,
     }

@@ -98,10 +98,17 @@ class PackedQ1:
         return self.biases is None
 
     def desc(self) -> _Weight:
+        """The C descriptor (rebuilt only when a tensor or shape changed)."""
+        key = (self.packed.data_ptr(), self.scales.data_ptr(),
+               None if self.biases is None else self.biases.data_ptr(), self.scales.dtype, self.N, self.K)
+        cached = self.__dict__.get("_desc_cache")
+        if cached is not None and cached[0] == key:
+            return cached[1]
         meta = _TORCH_TO_Q1.get(self.scales.dtype)
-        return _Weight(self.packed.data_ptr(), self.scales.data_ptr(),
-                       None if self.biases is None else self.biases.data_ptr(),
-                       -1 if meta is None else meta, 1 if self.biases is None else 0, self.N, self.K, 128, 0)
+        d = _Weight(key[0], key[1], key[2], -1 if meta is None else meta, 1 if self.biases is None else 0,
+                    self.N, self.K, 128, 0)
+        self.__dict__["_desc_cache"] = (key, d)
+        return d
 
     @staticmethod
     def from_host(w, device="cuda") -> "PackedQ1":
@@ -117,8 +124,15 @@ class PackedQ1:
         return PackedQ1(packed, scales, biases, int(w.N), int(w.K))
 
 
-def _stream() -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device=None) -> ctypes.c_void_p:
+    """The current HIP stream of `device` (default: the current device)."""
+    if _raw_stream is not None:
+        idx = torch.cuda.current_device() if device is None else device.index
+        return ctypes.c_void_p(_raw_stream(idx))
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
 class _Workspaces:
@@ -129,7 +143,7 @@ class _Workspaces:
         self._ws = {}
 
     def get(self, nbytes: int, device: torch.device) -> torch.Tensor:
-        key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+        key = (device.index, _stream(device).value)
         t = self._ws.get(key)
         if t is None or t.numel() < nbytes:
             t = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -157,6 +171,20 @@ def q1_qmm_workspace_bytes(M: int, w: PackedQ1) -> int:
     return n
 
 
+_need_cache = {}
+
+
+def _qmm_need(L, M: int, w: PackedQ1, d: _Weight) -> int:
+    key = (M, w.N, w.K, d.meta_dtype, d.symmetric)
+    n = _need_cache.get(key)
+    if n is None:
+        n = L.q1_qmm_workspace_bytes(M, ctypes.byref(d))
+        if n == 0 and L.q1_last_error():
+            raise Q1Error(1, L.q1_last_error().decode())
+        _need_cache[key] = n
+    return n
+
+
 def q1_qmm(x: torch.Tensor, w: PackedQ1, out_dtype: torch.dtype = torch.bfloat16,
            y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """``y[..., N] = x[..., K] @ W^T``; x bf16, leading dims flattened to M rows."""
@@ -170,12 +198,12 @@ def q1_qmm(x: torch.Tensor, w: PackedQ1, out_dtype: torch.dtype = torch.bfloat16
     _check_tensor(y, "y")
     L = load_library()
     d = w.desc()
-    need = L.q1_qmm_workspace_bytes(M, ctypes.byref(d))
+    need = _qmm_need(L, M, w, d) if M > 0 else 0
     ws = workspace if workspace is not None else (_WS.get(need, x.device) if need else None)
     _check(L.q1_qmm(ctypes.c_void_p(x.data_ptr()), _TORCH_TO_Q1.get(x.dtype, -1), M, ctypes.byref(d),
                     ctypes.c_void_p(y.data_ptr()), _TORCH_TO_Q1.get(y.dtype, -1),
                     None if ws is None else ctypes.c_void_p(ws.data_ptr()), 0 if ws is None else ws.numel(),
-                    _stream()))
+                    _stream(x.device)))
     return y
 
 
@@ -186,7 +214,7 @@ def q1_dequantize(w: PackedQ1, out_dtype: torch.dtype = torch.bfloat16,
     _check_tensor(out, "out")
     d = w.desc()
     _check(load_library().q1_dequantize(ctypes.byref(d), ctypes.c_void_p(out.data_ptr()),
-                                        _TORCH_TO_Q1.get(out.dtype, -1), _stream()))
+                                        _TORCH_TO_Q1.get(out.dtype, -1), _stream(out.device)))
     return out
 
 
@@ -202,7 +230,7 @@ def q1_embed_rows(ids: torch.Tensor, table: PackedQ1, out_dtype: torch.dtype = t
     d = table.desc()
     _check(load_library().q1_embed_rows(ctypes.c_void_p(ids.data_ptr()), 1 if ids.dtype == torch.int64 else 0, T,
                                         ctypes.byref(d), ctypes.c_void_p(out.data_ptr()),
-                                        _TORCH_TO_Q1.get(out.dtype, -1), _stream()))
+                                        _TORCH_TO_Q1.get(out.dtype, -1), _stream(out.device)))
     return out
 
 
@@ -227,7 +255,7 @@ def q1_ffn(x: torch.Tensor, gate: PackedQ1, up: PackedQ1, down: PackedQ1, y: Opt
     need = L.q1_ffn_workspace_bytes(M, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d))
     ws = workspace if workspace is not None else _WS.get(need, x.device)
     _check(L.q1_ffn(ctypes.c_void_p(x.data_ptr()), M, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
-                    ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
+                    ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(x.device)))
     if return_hidden:
         off = Q1_WS_RESERVED_BYTES
         h = ws[off:off + M * gate.N * 2].view(torch.bfloat16).view(*lead, gate.N).clone()
@@ -236,6 +264,7 @@ def q1_ffn(x: torch.Tensor, gate: PackedQ1, up: PackedQ1, down: PackedQ1, y: Opt
 
 
 def q1_set_max_packed_rows(rows: int) -> int:
+    _need_cache.clear()  # the routing, and with it the workspace sizes, change
     return load_library().q1_set_max_packed_rows(rows)
 
 
