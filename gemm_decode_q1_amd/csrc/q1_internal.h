@@ -100,6 +100,7 @@ struct MmaPlan {
   int P;           // workgroups per K segment
   int nb;          // tiles per wave
   int cgroup;      // S > 1: tiles per arrival counter
+  size_t red_bytes;  // LDS for the cross-wave sums
   int64_t wgs;     // S * P
   size_t lds_bytes;
   size_t partial_floats;  // S > 1: S*M*N*(pair ? 2 : 1)
@@ -118,6 +119,7 @@ struct MmaArgs {
   int64_t N;
   int32_t M, K, G, nspan;
   int32_t S, KSP, NWS, NWT, P, nb, cgroup;
+  uint32_t red_bytes;
   uint32_t x_bytes, packed_bytes, meta_bytes;
   int32_t out_dtype;
   void* out;

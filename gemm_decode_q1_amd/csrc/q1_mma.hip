@@ -79,6 +79,10 @@ constexpr int kOffCorr = kOffSc + 256;
 constexpr int kOffXs = kOffCorr + 256;
 constexpr int kSpanLds = kOffXs + 256;
 
+// per-wave LDS scratch of the word transpose: 16 rows x 34 dwords (32 used)
+constexpr int kScrStride = 34;
+constexpr int kScrDwords = 16 * kScrStride;
+
 constexpr uint32_t kBufWord3 = 0x00020000u;
 constexpr uint32_t kOOB = 0x80000000u;
 
@@ -249,45 +253,49 @@ __device__ __forceinline__ void transpose_quarters(u32x4& w) {
   w[3] = r23[1];
 }
 
-// Scales (or biases) of one row for the 4 groups of a span, one register each.
-// Groups past the end read 0.
-// (Each value stays in its own register until use: combining two 16-bit
-// loads right after issue would make the wave wait for them.)
-// With G % 4 == 0 the 4 values are one aligned 8-byte load (two registers of
-// packed 16-bit values); otherwise 4 loads of 16 bits, one register each.
-template <bool SC64>
-__device__ __forceinline__ void load_meta4(__amdgpu_buffer_rsrc_t r, bool rowok, uint32_t row_off, int G, int g0,
+// Scales (or biases) of one row for the 8 groups of a double span, packed as
+// 16-bit values two per register.  With G % 8 == 0 they are one aligned
+// 16-byte load; otherwise 8 loads of 16 bits (groups past the end read 0).
+// (The 16-bit loads are combined only at use: combining them right after
+// issue would make the wave wait for them.)
+template <bool SC128>
+__device__ __forceinline__ void load_meta8(__amdgpu_buffer_rsrc_t r, bool rowok, uint32_t row_off, int G, int g0,
                                            uint32_t* v) {
-  if (SC64) {
-    const uint32_t o = (row_off + (uint32_t)g0 * 2) | (rowok ? 0u : kOOB);
-    const auto d = __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0);
-    v[0] = d[0];
-    v[1] = d[1];
+  if (SC128) {
+    const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(r, (row_off + (uint32_t)g0 * 2) | (rowok ? 0u : kOOB), 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = d[i];
   } else {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < 8; ++g) {
       const uint32_t o = (row_off + (uint32_t)(g0 + g) * 2) | ((rowok && g0 + g < G) ? 0u : kOOB);
       v[g] = __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, 0);
     }
   }
 }
 
-template <bool MBF16, bool SC64>
+template <bool MBF16, bool SC128>
 __device__ __forceinline__ float meta_at(const uint32_t* v, int g) {
-  if (SC64) return meta_f32<MBF16>((g & 1) ? (v[g >> 1] >> 16) : (v[g >> 1] & 0xffffu));
+  if (SC128) return meta_f32<MBF16>((g & 1) ? (v[g >> 1] >> 16) : (v[g >> 1] & 0xffffu));
   return meta_f32<MBF16>(v[g]);
 }
 
 // Work of a wave: tiles k = 0, 1, .. of its column (tile ((k*P + p)*NWT + wt):
 // consecutive tiles of a wave are P*NWT tiles apart, so the last round
-// spreads evenly), and for each tile the spans [sp_lo, sp_hi) of its slice of
-// the segment, spans inner: a tile's 16 rows are contiguous in memory, so the
-// loads in flight cover a compact block.  Item i = (tile k, span s) sits in
-// ring slot i % D; its loads are issued D items ahead.
-template <bool AFFINE, bool MBF16, bool PAIR, bool SC64>
+// spreads evenly), and for each tile the double spans (8 groups, 128 bytes of
+// every row) [ds_lo, ds_hi) of its slice of the segment.  Item i = (tile k,
+// double span d) sits in ring slot i % D; its loads are issued D items ahead.
+//
+// Loads: instruction h of an item reads rows 8h..8h+7 of the tile, lane l the
+// 16 bytes (group l%8, 4 words) of row l/8, so each row's 128 bytes come from
+// 8 neighbouring lanes.  The MFMA B operand wants lane (n, q) = word q of every
+// group of row n: the words go through a per-wave LDS scratch (row stride 34
+// dwords: the 8-byte writes and 4-byte reads are bank-conflict free).
+template <bool AFFINE, bool MBF16, bool PAIR, bool SC128>
 __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   constexpr int NMAT = PAIR ? 2 : 1;
-  constexpr int D = 8;
+  constexpr int D = PAIR ? 2 : 4;
+  constexpr int NSC = SC128 ? 4 : 8;  // registers of metadata per row and item
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int last_flag;
 
@@ -296,119 +304,135 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seg = (int)(blockIdx.x % (unsigned)a.S);
   const int p = (int)(blockIdx.x / (unsigned)a.S);
-  const int span0 = seg * a.KSP;
+  const int span0 = seg * a.KSP;                                    // even
   const int nsp = (span0 + a.KSP <= a.nspan) ? a.KSP : a.nspan - span0;
+  const int nds = (nsp + 1) >> 1;                                   // double spans of the segment
   const int ws = wave % a.NWS, wt = wave / a.NWS;
-  const int sp_lo = (ws * nsp) / a.NWS, sp_hi = ((ws + 1) * nsp) / a.NWS;
-  const int nspw = sp_hi - sp_lo;  // >= 1: the plan keeps NWS <= spans of every segment
-  const int nitems = a.nb * nspw;  // a.nb = tiles per wave
+  const int ds_lo = (ws * nds) / a.NWS, ds_hi = ((ws + 1) * nds) / a.NWS;
+  const int ndw = ds_hi - ds_lo;  // >= 1: the plan keeps NWS <= double spans of every segment
+  const int nitems = a.nb * ndw;  // a.nb = tiles per wave
   float* red = reinterpret_cast<float*>(lds + (size_t)a.KSP * kSpanLds);
+  uint32_t* scr = reinterpret_cast<uint32_t*>(lds + (size_t)a.KSP * kSpanLds + (size_t)a.red_bytes) +
+                  wave * (NMAT * kScrDwords);
 
   const __amdgpu_buffer_rsrc_t rp[2] = {rsrc(a.p0, a.packed_bytes), rsrc(PAIR ? a.p1 : a.p0, a.packed_bytes)};
   const __amdgpu_buffer_rsrc_t rs[2] = {rsrc(a.s0, a.meta_bytes), rsrc(PAIR ? a.s1 : a.s0, a.meta_bytes)};
   const __amdgpu_buffer_rsrc_t rbias[2] = {rsrc(AFFINE ? a.b0 : a.s0, a.meta_bytes),
                                            rsrc(AFFINE && PAIR ? a.b1 : a.s0, a.meta_bytes)};
 
-  const int nl = lane & 15;  // weight row within a tile (B and D column)
-  const int q = lane >> 4;   // lane quarter
+  const int nl = lane & 15;   // weight row within a tile (B and D column)
+  const int q = lane >> 4;    // lane quarter
+  const int lr = lane >> 3;   // row within a load instruction
+  const int lc = lane & 7;    // 16-byte chunk (group) within a row's 128 bytes
   const uint32_t row_bytes = (uint32_t)a.K >> 3;
-  const uint32_t q16 = (uint32_t)q * 16u;
   // row indices fit in 31 bits (the plan keeps N*K/8 below 2^31)
   const int Nrows = (int)a.N;
   auto tile_of = [&](int k) -> int { return (k * a.P + p) * a.NWT + wt; };
 
-  u32x4 words[D][NMAT];
-  uint32_t sreg[D][NMAT][4];
-  uint32_t breg[D][NMAT][4];
+  u32x4 words[D][NMAT][2];
+  uint32_t sreg[D][NMAT][NSC];
+  uint32_t breg[D][NMAT][NSC];
   float acc[NMAT][4];
 #pragma unroll
   for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0f;
 
-  // issue the loads of item (tile k, span s) into slot u
-  auto issue = [&](int u, int k, int sidx, bool ok) {
-    const int span = span0 + sp_lo + sidx;
+  // issue the loads of item (tile k, double span didx) into slot u
+  auto issue = [&](int u, int k, int didx, bool ok) {
+    const int sp = span0 + 2 * (ds_lo + didx);  // first span of the double span
+    const int r0 = tile_of(k) * 16 + lr;
+    const int g = 4 * sp + lc;                  // this lane's group
+    const uint32_t col = (uint32_t)(sp * 64) + (uint32_t)lc * 16u;
+    const bool gok = ok && g < a.G;
+    const uint32_t o0 = ((uint32_t)r0 * row_bytes + col) | ((gok && r0 < Nrows) ? 0u : kOOB);
+    const uint32_t o1 = ((uint32_t)(r0 + 8) * row_bytes + col) | ((gok && r0 + 8 < Nrows) ? 0u : kOOB);
     const int n = tile_of(k) * 16 + nl;
-    const bool rowok = ok && n < Nrows;
-    // out-of-range lanes get bit 31 set (past every buffer): no branches
-    const uint32_t wo = ((uint32_t)n * row_bytes + (uint32_t)(span * 64) + q16) |
-                        ((rowok && 4 * span + q < a.G) ? 0u : kOOB);
+    const bool nok = ok && n < Nrows;
     const uint32_t mo = (uint32_t)n * (uint32_t)a.G * 2u;
 #pragma unroll
     for (int mt = 0; mt < NMAT; ++mt) {
-      words[u][mt] = __builtin_amdgcn_raw_buffer_load_b128(rp[mt], wo, 0, 2);
-      load_meta4<SC64>(rs[mt], rowok, mo, a.G, 4 * span, sreg[u][mt]);
-      if (AFFINE) load_meta4<SC64>(rbias[mt], rowok, mo, a.G, 4 * span, breg[u][mt]);
+      words[u][mt][0] = __builtin_amdgcn_raw_buffer_load_b128(rp[mt], o0, 0, 2);
+      words[u][mt][1] = __builtin_amdgcn_raw_buffer_load_b128(rp[mt], o1, 0, 2);
+      load_meta8<SC128>(rs[mt], nok, mo, a.G, 4 * sp, sreg[u][mt]);
+      if (AFFINE) load_meta8<SC128>(rbias[mt], nok, mo, a.G, 4 * sp, breg[u][mt]);
     }
   };
 
   // activation loads first, then the first D items of weights, then the
   // conversion (which waits for the activations only)
   PrepLoads pl;
-  prep_load(a, span0, nsp, tid, pl);
+  prep_load(a, span0, 2 * nds, tid, pl);
   {
-    int k = 0, sidx = 0;
+    int k = 0, didx = 0;
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      issue(u, k, sidx, u < nitems);
-      if (++sidx == nspw) {
-        sidx = 0;
+      issue(u, k, didx, u < nitems);
+      if (++didx == ndw) {
+        didx = 0;
         ++k;
       }
     }
   }
-  prep_compute<AFFINE>(a, nsp, lds, tid, pl);
+  prep_compute<AFFINE>(a, 2 * nds, lds, tid, pl);
   lds_barrier();
 
-  // A rows: lane's row m' = lane % 16 carries activation row m' % 8 (hi for
-  // m' < 8, lo for m' >= 8); only rows of activation index < M are read.
-  const bool arow = (nl & 7) < a.M;
-
-  auto compute = [&](int u, int spl) {
-    const unsigned char* base = lds + (sp_lo + spl) * kSpanLds;
-    const uint32_t scale_a = reinterpret_cast<const uint32_t*>(base + kOffSc)[lane];
-    v8i A[4];
-    v4f C[4], XS[4];
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      u32x4 h0 = {0u, 0u, 0u, 0u}, h1 = {0u, 0u, 0u, 0u};
-      if (arow) {
-        h0 = reinterpret_cast<const u32x4*>(base + (g4 * 8) * 256)[lane];
-        h1 = reinterpret_cast<const u32x4*>(base + (g4 * 8 + 4) * 256)[lane];
-      }
-      A[g4] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-      C[g4] = reinterpret_cast<const v4f*>(base + kOffCorr)[g4 * 4 + q];
-      if (AFFINE) XS[g4] = reinterpret_cast<const v4f*>(base + kOffXs)[g4 * 4 + q];
-    }
+  auto compute = [&](int u, int didx) {
+    // B words of all groups: lane (n, q) gets word q of groups 0..7 of row n
+    uint32_t bw[NMAT][8];
 #pragma unroll
     for (int mt = 0; mt < NMAT; ++mt) {
-      u32x4 w = words[u][mt];
-      transpose_quarters(w);
-      v4f Dg[4];
+      uint32_t* t = scr + mt * kScrDwords;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const uint32_t wd = w[g4];
-        const v8i B = {(int)(wd & 0x11111111u), (int)(wd & 0x22222222u), (int)(wd & 0x44444444u),
-                       (int)((wd & 0x88888888u) | 0x22222222u), 0, 0, 0, 0};
-        if (g4 == 0)
-          Dg[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, C[0], 0, 4, 0, (int)scale_a, 0, 0x7f7f7f7f);
-        else if (g4 == 1)
-          Dg[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, C[1], 0, 4, 1, (int)scale_a, 0, 0x7f7f7f7f);
-        else if (g4 == 2)
-          Dg[2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, C[2], 0, 4, 2, (int)scale_a, 0, 0x7f7f7f7f);
-        else
-          Dg[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[3], B, C[3], 0, 4, 3, (int)scale_a, 0, 0x7f7f7f7f);
+      for (int h = 0; h < 2; ++h) {
+        uint2* dst = reinterpret_cast<uint2*>(t + (8 * h + lr) * kScrStride + 4 * lc);
+        dst[0] = uint2{words[u][mt][h][0], words[u][mt][h][1]};
+        dst[1] = uint2{words[u][mt][h][2], words[u][mt][h][3]};
       }
 #pragma unroll
+      for (int g = 0; g < 8; ++g) bw[mt][g] = t[nl * kScrStride + 4 * g + q];
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const unsigned char* base = lds + (2 * (ds_lo + didx) + half) * kSpanLds;
+      const uint32_t scale_a = reinterpret_cast<const uint32_t*>(base + kOffSc)[lane];
+      v8i A[4];
+      v4f C[4], XS[4];
+#pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const float sv = meta_at<MBF16, SC64>(sreg[u][mt], g4);
+        const u32x4 h0 = reinterpret_cast<const u32x4*>(base + (g4 * 8) * 256)[lane];
+        const u32x4 h1 = reinterpret_cast<const u32x4*>(base + (g4 * 8 + 4) * 256)[lane];
+        A[g4] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+        C[g4] = reinterpret_cast<const v4f*>(base + kOffCorr)[g4 * 4 + q];
+        if (AFFINE) XS[g4] = reinterpret_cast<const v4f*>(base + kOffXs)[g4 * 4 + q];
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(sv, Dg[g4][i], acc[mt][i]);
-        if (AFFINE) {
-          const float bv = meta_at<MBF16, SC64>(breg[u][mt], g4);
+      for (int mt = 0; mt < NMAT; ++mt) {
+        v4f Dg[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(bv, XS[g4][i], acc[mt][i]);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const uint32_t wd = bw[mt][4 * half + g4];
+          const v8i B = {(int)(wd & 0x11111111u), (int)(wd & 0x22222222u), (int)(wd & 0x44444444u),
+                         (int)((wd & 0x88888888u) | 0x22222222u), 0, 0, 0, 0};
+          if (g4 == 0)
+            Dg[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, C[0], 0, 4, 0, (int)scale_a, 0, 0x7f7f7f7f);
+          else if (g4 == 1)
+            Dg[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, C[1], 0, 4, 1, (int)scale_a, 0, 0x7f7f7f7f);
+          else if (g4 == 2)
+            Dg[2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, C[2], 0, 4, 2, (int)scale_a, 0, 0x7f7f7f7f);
+          else
+            Dg[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[3], B, C[3], 0, 4, 3, (int)scale_a, 0, 0x7f7f7f7f);
+        }
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float sv = meta_at<MBF16, SC128>(sreg[u][mt], 4 * half + g4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(sv, Dg[g4][i], acc[mt][i]);
+          if (AFFINE) {
+            const float bv = meta_at<MBF16, SC128>(breg[u][mt], 4 * half + g4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(bv, XS[g4][i], acc[mt][i]);
+          }
         }
       }
     }
@@ -438,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0f;
     }
-    if (a.NWS == 1) {  // (the plan uses one K segment here)
+    if (a.NWS == 1 && a.S == 1) {
       const int row = tile_of(k) * 16 + nl;
       const int mA = 4 * ((lane >> 4) & 1) + (lane >> 5);
       if (row < Nrows) {
@@ -466,33 +490,32 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   // their tile index is >= nb, so they emit nothing): a loop body without
   // early exits keeps the ring in place across iterations.
   const int nitems_pad = (nitems + D - 1) / D * D;
-  int k = 0, sidx = 0;    // current item
-  int ik = 0, isidx = 0;  // item + D (next loads)
-  isidx = D;
-  while (isidx >= nspw) {
-    isidx -= nspw;
+  int k = 0, didx = 0;    // current item
+  int ik = 0, iidx = D;   // item + D (next loads)
+  while (iidx >= ndw) {
+    iidx -= ndw;
     ++ik;
   }
   for (int base = 0; base < nitems_pad; base += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      compute(u, sidx);
-      issue(u, ik, isidx, base + u + D < nitems);
+      compute(u, didx);
+      issue(u, ik, iidx, base + u + D < nitems);
       __builtin_amdgcn_sched_barrier(0);  // keep items apart: bounded register use
-      if (sidx == nspw - 1 && k < a.nb) tile_done(k);
-      if (++sidx == nspw) {
-        sidx = 0;
+      if (didx == ndw - 1 && k < a.nb) tile_done(k);
+      if (++didx == ndw) {
+        didx = 0;
         ++k;
       }
-      if (++isidx == nspw) {
-        isidx = 0;
+      if (++iidx == ndw) {
+        iidx = 0;
         ++ik;
       }
     }
   }
-  if (a.NWS == 1) return;
+  if (a.NWS == 1 && a.S == 1) return;
 
-  // ---- the waves of the segment's spans meet: sum over ws in order ----
+  // ---- the waves of the segment's double spans meet: sum over ws in order ----
   lds_barrier();
   const int nout = a.NWT * a.nb * 128;
   for (int o = tid; o < nout; o += kThreads) {
@@ -519,8 +542,8 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   }
   if (a.S == 1) return;
 
-  // ---- split K (NWT == 1): the last of the S workgroups with this p adds
-  // the partials of p's tiles in segment order ----
+  // ---- split K: the last of the S workgroups with this p adds the
+  // partials of p's tiles in segment order ----
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are performed
   lds_barrier();
   if (tid == 0) {
@@ -529,11 +552,13 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   }
   lds_barrier();
   if (!last_flag) return;
-  const int nfin = a.nb * 16 * a.M;
+  const int per_m = a.NWT * a.nb * 16;
+  const int nfin = per_m * a.M;
   for (int o = tid; o < nfin; o += kThreads) {
-    const int m = o / (a.nb * 16), rem = o - m * (a.nb * 16);
-    const int k2 = rem >> 4;
-    const int row = (k2 * a.P + p) * 16 + (rem & 15);
+    const int m = o / per_m, rem = o - m * per_m;
+    const int wt2 = rem / (a.nb * 16), rem2 = rem - wt2 * (a.nb * 16);
+    const int k2 = rem2 >> 4;
+    const int row = ((k2 * a.P + p) * a.NWT + wt2) * 16 + (rem2 & 15);
     if (row >= Nrows) continue;
     float v[NMAT];
 #pragma unroll
@@ -562,20 +587,20 @@ int device_cus() {
   return cus;
 }
 
-template <bool AFFINE, bool MBF16, bool PAIR, bool SC64>
+template <bool AFFINE, bool MBF16, bool PAIR, bool SC128>
 hipError_t launch_k(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&q1_mma_kernel<AFFINE, MBF16, PAIR, SC64>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&q1_mma_kernel<AFFINE, MBF16, PAIR, SC128>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 64);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((q1_mma_kernel<AFFINE, MBF16, PAIR, SC64>), dim3((unsigned)p.wgs), dim3(kThreads), p.lds_bytes,
+  hipLaunchKernelGGL((q1_mma_kernel<AFFINE, MBF16, PAIR, SC128>), dim3((unsigned)p.wgs), dim3(kThreads), p.lds_bytes,
                      s, a);
   return hipGetLastError();
 }
 
 template <bool AFFINE, bool MBF16, bool PAIR>
 hipError_t launch_t(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
-  return (a.G % 4 == 0) ? launch_k<AFFINE, MBF16, PAIR, true>(p, a, s) : launch_k<AFFINE, MBF16, PAIR, false>(p, a, s);
+  return (a.G % 8 == 0) ? launch_k<AFFINE, MBF16, PAIR, true>(p, a, s) : launch_k<AFFINE, MBF16, PAIR, false>(p, a, s);
 }
 
 }  // namespace
@@ -602,20 +627,20 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, c
   p->G = (int)(K / 128);
   p->nspan = (p->G + 3) / 4;
   p->ntiles = (N + 15) / 16;
-  p->S = (p->nspan + kKspMax - 1) / kKspMax;
-  p->KSP = (p->nspan + p->S - 1) / p->S;
-  p->S = (p->nspan + p->KSP - 1) / p->KSP;
-  const int last_seg = p->nspan - (p->S - 1) * p->KSP;  // spans of the shortest segment
+  const int ndsp = (p->nspan + 1) / 2;  // double spans
+  const int kdmax = kKspMax / 2;
+  p->S = (ndsp + kdmax - 1) / kdmax;
+  int kds = (ndsp + p->S - 1) / p->S;
+  p->S = (ndsp + kds - 1) / kds;
+  p->KSP = 2 * kds;
+  const int last_seg = ndsp - (p->S - 1) * kds;  // double spans of the shortest segment
   // With few tiles per CU (or a split K) the waves of a workgroup share its
-  // tiles and split the segment's spans; otherwise each wave owns whole tiles.
+  // tiles and split the segment's double spans; otherwise each wave owns
+  // whole tiles.
   const int64_t tiles_per_cu = (p->ntiles * p->S + cus - 1) / cus;
   int nws = 1;
   if (p->S > 1 || tiles_per_cu < 2 * kNW)
     while (nws * 2 <= kNW && nws * 2 <= last_seg) nws *= 2;
-  if (p->S > 1 && nws != kNW) {
-    *why = "split K needs at least 8 spans per segment";
-    return false;
-  }
   p->NWS = nws;
   p->NWT = kNW / nws;
   p->TB = 1;
@@ -625,13 +650,14 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, c
   p->P = (int)P;
   p->nb = (int)((p->ntiles + P * p->NWT - 1) / (P * p->NWT));  // tiles per wave
   p->wgs = (int64_t)p->S * P;
-  p->lds_bytes = (size_t)p->KSP * kSpanLds + (nws > 1 ? (size_t)kNW * p->nb * nmat * 512 : 0);
-  if ((int64_t)M * p->KSP * 32 > (int64_t)kPrepRounds * kThreads) {
-    *why = "activation conversion exceeds its register rounds";
-    return false;
-  }
+  p->red_bytes = (nws > 1 || p->S > 1) ? (size_t)kNW * p->nb * nmat * 512 : 0;
+  p->lds_bytes = (size_t)p->KSP * kSpanLds + p->red_bytes + (size_t)kNW * nmat * kScrDwords * 4;
   if (p->lds_bytes > 160 * 1024 - 64) {
     *why = "LDS budget exceeded";
+    return false;
+  }
+  if ((int64_t)M * p->KSP * 32 > (int64_t)kPrepRounds * kThreads) {
+    *why = "activation conversion exceeds its register rounds";
     return false;
   }
   p->cgroup = 1;
@@ -663,6 +689,7 @@ hipError_t launch_mma(const MmaPlan& p, const uint16_t* x, int64_t x_ld, const Q
   g.P = p.P;
   g.nb = p.nb;
   g.cgroup = p.cgroup;
+  g.red_bytes = (uint32_t)p.red_bytes;
   g.x_bytes = (uint32_t)(((p.M - 1) * x_ld + a.K) * 2);
   g.packed_bytes = (uint32_t)(a.N * (a.K / 8));
   g.meta_bytes = (uint32_t)(a.N * (a.K / 128) * 2);
