@@ -280,11 +280,15 @@ __device__ __forceinline__ float meta_at(const uint32_t* v, int g) {
   return meta_f32<MBF16>(v[g]);
 }
 
-// Work of a wave: tiles k = 0, 1, .. of its column (tile ((k*P + p)*NWT + wt):
-// consecutive tiles of a wave are P*NWT tiles apart, so the last round
-// spreads evenly), and for each tile the double spans (8 groups, 128 bytes of
-// every row) [ds_lo, ds_hi) of its slice of the segment.  Item i = (tile k,
-// double span d) sits in ring slot i % D; its loads are issued D items ahead.
+// Work.  Workgroup p of K segment `seg` owns tiles p, p + P, p + 2P, .. (16
+// rows each; consecutive tiles go to different workgroups) and the segment's
+// double spans (8 groups, 128 bytes of every row).  Its items (local tile k,
+// double span d), tiles outer, are split evenly over its 8 waves: wave w takes
+// items [w*I/8, (w+1)*I/8).  A tile that lies inside one wave's range is stored
+// by that wave straight from registers; the (at most two) partial tiles at the
+// ends of each wave's range meet in LDS after the loop and are added in wave
+// order.  Item i of a wave sits in ring slot i % D; its loads are issued D
+// items ahead.
 //
 // Loads: instruction h of an item reads rows 8h..8h+7 of the tile, lane l the
 // 16 bytes (group l%8, 4 words) of row l/8, so each row's 128 bytes come from
@@ -307,11 +311,12 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   const int span0 = seg * a.KSP;                                    // even
   const int nsp = (span0 + a.KSP <= a.nspan) ? a.KSP : a.nspan - span0;
   const int nds = (nsp + 1) >> 1;                                   // double spans of the segment
-  const int ws = wave % a.NWS, wt = wave / a.NWS;
-  const int ds_lo = (ws * nds) / a.NWS, ds_hi = ((ws + 1) * nds) / a.NWS;
-  const int ndw = ds_hi - ds_lo;  // >= 1: the plan keeps NWS <= double spans of every segment
-  const int nitems = a.nb * ndw;  // a.nb = tiles per wave
-  float* red = reinterpret_cast<float*>(lds + (size_t)a.KSP * kSpanLds);
+  const int ntiles = (int)((a.N + 15) >> 4);
+  const int nbp = (ntiles - p + a.P - 1) / a.P;                     // tiles of this workgroup
+  const int I = nbp * nds;                                          // items of this workgroup
+  const int i0 = (wave * I) / kNW, i1 = ((wave + 1) * I) / kNW;
+  const int nitems = i1 - i0;
+  float* red = reinterpret_cast<float*>(lds + (size_t)a.KSP * kSpanLds);  // [w][slot][mt][ab][64]
   uint32_t* scr = reinterpret_cast<uint32_t*>(lds + (size_t)a.KSP * kSpanLds + (size_t)a.red_bytes) +
                   wave * (NMAT * kScrDwords);
 
@@ -327,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   const uint32_t row_bytes = (uint32_t)a.K >> 3;
   // row indices fit in 31 bits (the plan keeps N*K/8 below 2^31)
   const int Nrows = (int)a.N;
-  auto tile_of = [&](int k) -> int { return (k * a.P + p) * a.NWT + wt; };
+  auto tile_of = [&](int k) -> int { return k * a.P + p; };
 
   u32x4 words[D][NMAT][2];
   uint32_t sreg[D][NMAT][NSC];
@@ -338,11 +343,11 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0f;
 
-  // issue the loads of item (tile k, double span didx) into slot u
-  auto issue = [&](int u, int k, int didx, bool ok) {
-    const int sp = span0 + 2 * (ds_lo + didx);  // first span of the double span
+  // issue the loads of item (local tile k, double span d) into slot u
+  auto issue = [&](int u, int k, int d, bool ok) {
+    const int sp = span0 + 2 * d;  // first span of the double span
     const int r0 = tile_of(k) * 16 + lr;
-    const int g = 4 * sp + lc;                  // this lane's group
+    const int g = 4 * sp + lc;     // this lane's group
     const uint32_t col = (uint32_t)(sp * 64) + (uint32_t)lc * 16u;
     const bool gok = ok && g < a.G;
     const uint32_t o0 = ((uint32_t)r0 * row_bytes + col) | ((gok && r0 < Nrows) ? 0u : kOOB);
@@ -364,12 +369,12 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   PrepLoads pl;
   prep_load(a, span0, 2 * nds, tid, pl);
   {
-    int k = 0, didx = 0;
+    int k = i0 / (nds > 0 ? nds : 1), d = i0 - k * nds;
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      issue(u, k, didx, u < nitems);
-      if (++didx == ndw) {
-        didx = 0;
+      issue(u, k, d, u < nitems);
+      if (++d == nds) {
+        d = 0;
         ++k;
       }
     }
@@ -377,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   prep_compute<AFFINE>(a, 2 * nds, lds, tid, pl);
   lds_barrier();
 
-  auto compute = [&](int u, int didx) {
+  auto compute = [&](int u, int d) {
     // B words of all groups: lane (n, q) gets word q of groups 0..7 of row n
     uint32_t bw[NMAT][8];
 #pragma unroll
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const unsigned char* base = lds + (2 * (ds_lo + didx) + half) * kSpanLds;
+      const unsigned char* base = lds + (2 * d + half) * kSpanLds;
       const uint32_t scale_a = reinterpret_cast<const uint32_t*>(base + kOffSc)[lane];
       v8i A[4];
       v4f C[4], XS[4];
@@ -438,17 +443,27 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
     }
   };
 
-  auto final_store = [&](int m, int row, const float* v) {
-    if (PAIR)
-      static_cast<uint16_t*>(a.out)[m * a.out_ld + row] = (uint16_t)f32_to_bf16_bits(silu_f32(v[0]) * v[1]);
-    else
-      store_out(a.out, a.out_dtype, m * a.out_ld + row, v[0]);
+  // one result (activation row m, weight row `row`): the output, or with a
+  // split K the segment's partial sum
+  auto emit = [&](int m, int row, const float* v) {
+    if (a.S == 1) {
+      if (PAIR)
+        static_cast<uint16_t*>(a.out)[m * a.out_ld + row] = (uint16_t)f32_to_bf16_bits(silu_f32(v[0]) * v[1]);
+      else
+        store_out(a.out, a.out_dtype, m * a.out_ld + row, v[0]);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt)
+        __hip_atomic_store(&a.partial[(((int64_t)seg * a.M + m) * NMAT + mt) * a.N + row], v[mt], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
   };
 
-  // After tile k: lane l of half ab holds activation row
-  // 4*((l>>4)&1) + 2*ab + (l>>5) of weight row l & 15 (hi + lo combined).
-  // A wave that owns whole tiles stores them; otherwise the result waits in
-  // LDS (red[ws][wt][k][mt][ab][64]) for the reduction after the loop.
+  // End of this wave's part of local tile k: lane l of half ab holds
+  // activation row 4*((l>>4)&1) + 2*ab + (l>>5) of weight row l & 15 (hi + lo
+  // combined).  A whole tile is emitted; a partial one goes to LDS slot
+  // (wave, k == first tile ? 0 : 1).
+  const int kfirst = i0 / (nds > 0 ? nds : 1);
   auto tile_done = [&](int k) {
     float comb[NMAT][2];
 #pragma unroll
@@ -462,7 +477,8 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0f;
     }
-    if (a.NWS == 1 && a.S == 1) {
+    const bool whole = k * nds >= i0 && (k + 1) * nds <= i1;
+    if (whole) {
       const int row = tile_of(k) * 16 + nl;
       const int mA = 4 * ((lane >> 4) & 1) + (lane >> 5);
       if (row < Nrows) {
@@ -473,72 +489,69 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
             float v[NMAT];
 #pragma unroll
             for (int mt = 0; mt < NMAT; ++mt) v[mt] = comb[mt][ab];
-            final_store(m, row, v);
+            emit(m, row, v);
           }
         }
       }
     } else {
+      const int slot = (k == kfirst) ? 0 : 1;
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-        for (int ab = 0; ab < 2; ++ab)
-          red[((((ws * a.NWT + wt) * a.nb + k) * NMAT + mt) * 2 + ab) * 64 + lane] = comb[mt][ab];
+        for (int ab = 0; ab < 2; ++ab) red[(((wave * 2 + slot) * NMAT + mt) * 2 + ab) * 64 + lane] = comb[mt][ab];
     }
   };
 
-  // Whole turns of the ring (items past the end load nothing and add zeros;
-  // their tile index is >= nb, so they emit nothing): a loop body without
-  // early exits keeps the ring in place across iterations.
+  // Whole turns of the ring (items past the end load nothing and add zeros
+  // and end no tile): a loop body without early exits keeps the ring in place
+  // across iterations.
   const int nitems_pad = (nitems + D - 1) / D * D;
-  int k = 0, didx = 0;    // current item
-  int ik = 0, iidx = D;   // item + D (next loads)
-  while (iidx >= ndw) {
-    iidx -= ndw;
+  int k = kfirst, d = i0 - kfirst * nds;  // current item
+  int ik = k, id = d + D;                 // item + D (next loads)
+  while (nds > 0 && id >= nds) {
+    id -= nds;
     ++ik;
   }
   for (int base = 0; base < nitems_pad; base += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      compute(u, didx);
-      issue(u, ik, iidx, base + u + D < nitems);
+      compute(u, d);
+      issue(u, ik, id, base + u + D < nitems);
       __builtin_amdgcn_sched_barrier(0);  // keep items apart: bounded register use
-      if (didx == ndw - 1 && k < a.nb) tile_done(k);
-      if (++didx == ndw) {
-        didx = 0;
+      if (base + u < nitems && (d == nds - 1 || base + u == nitems - 1)) tile_done(k);
+      if (++d == nds) {
+        d = 0;
         ++k;
       }
-      if (++iidx == ndw) {
-        iidx = 0;
+      if (++id == nds) {
+        id = 0;
         ++ik;
       }
     }
   }
-  if (a.NWS == 1 && a.S == 1) return;
 
-  // ---- the waves of the segment's double spans meet: sum over ws in order ----
+  // ---- partial tiles: contributions of consecutive waves, in wave order ----
   lds_barrier();
-  const int nout = a.NWT * a.nb * 128;
-  for (int o = tid; o < nout; o += kThreads) {
-    const int wt2 = o / (a.nb * 128), rem = o - wt2 * (a.nb * 128);
-    const int k2 = rem >> 7, r = rem & 127, ab = r >> 6, l = r & 63;
+  for (int o = tid; o < nbp * 128; o += kThreads) {
+    const int kk = o >> 7, r = o & 127, ab = r >> 6, l = r & 63;
+    const int t0 = kk * nds, t1 = t0 + nds;  // the tile's items
+    int wa = 0;
+    while (((wa + 1) * I) / kNW <= t0) ++wa;  // wave holding item t0
+    if ((wa * I) / kNW <= t0 && ((wa + 1) * I) / kNW >= t1) continue;  // whole in one wave: emitted
     const int m = 4 * ((l >> 4) & 1) + 2 * ab + (l >> 5);
-    const int row = ((k2 * a.P + p) * a.NWT + wt2) * 16 + (l & 15);
+    const int row = tile_of(kk) * 16 + (l & 15);
     if (m >= a.M || row >= Nrows) continue;
     float v[NMAT];
 #pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) {
-      float sum = 0.0f;
-      for (int w2 = 0; w2 < a.NWS; ++w2) sum += red[((((w2 * a.NWT + wt2) * a.nb + k2) * NMAT + mt) * 2 + ab) * 64 + l];
-      v[mt] = sum;
-    }
-    if (a.S == 1) {
-      final_store(m, row, v);
-    } else {
+    for (int mt = 0; mt < NMAT; ++mt) v[mt] = 0.0f;
+    for (int w2 = wa; w2 < kNW && (w2 * I) / kNW < t1; ++w2) {
+      const int w_i0 = (w2 * I) / kNW;
+      if (((w2 + 1) * I) / kNW == w_i0) continue;  // wave without items
+      const int slot = (kk == w_i0 / nds) ? 0 : 1;
 #pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt)
-        __hip_atomic_store(&a.partial[(((int64_t)seg * a.M + m) * NMAT + mt) * a.N + row], v[mt], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      for (int mt = 0; mt < NMAT; ++mt) v[mt] += red[(((w2 * 2 + slot) * NMAT + mt) * 2 + ab) * 64 + l];
     }
+    emit(m, row, v);
   }
   if (a.S == 1) return;
 
@@ -552,13 +565,10 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   }
   lds_barrier();
   if (!last_flag) return;
-  const int per_m = a.NWT * a.nb * 16;
-  const int nfin = per_m * a.M;
-  for (int o = tid; o < nfin; o += kThreads) {
+  const int per_m = nbp * 16;
+  for (int o = tid; o < per_m * a.M; o += kThreads) {
     const int m = o / per_m, rem = o - m * per_m;
-    const int wt2 = rem / (a.nb * 16), rem2 = rem - wt2 * (a.nb * 16);
-    const int k2 = rem2 >> 4;
-    const int row = ((k2 * a.P + p) * a.NWT + wt2) * 16 + (rem2 & 15);
+    const int row = tile_of(rem >> 4) * 16 + (rem & 15);
     if (row >= Nrows) continue;
     float v[NMAT];
 #pragma unroll
@@ -569,7 +579,10 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
                                  __HIP_MEMORY_SCOPE_AGENT);
       v[mt] = sum;
     }
-    final_store(m, row, v);
+    if (PAIR)
+      static_cast<uint16_t*>(a.out)[m * a.out_ld + row] = (uint16_t)f32_to_bf16_bits(silu_f32(v[0]) * v[1]);
+    else
+      store_out(a.out, a.out_dtype, m * a.out_ld + row, v[0]);
   }
   if (tid == 0) __hip_atomic_store(&a.counters[p], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -630,27 +643,19 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, c
   const int ndsp = (p->nspan + 1) / 2;  // double spans
   const int kdmax = kKspMax / 2;
   p->S = (ndsp + kdmax - 1) / kdmax;
-  int kds = (ndsp + p->S - 1) / p->S;
+  const int kds = (ndsp + p->S - 1) / p->S;
   p->S = (ndsp + kds - 1) / kds;
   p->KSP = 2 * kds;
-  const int last_seg = ndsp - (p->S - 1) * kds;  // double spans of the shortest segment
-  // With few tiles per CU (or a split K) the waves of a workgroup share its
-  // tiles and split the segment's double spans; otherwise each wave owns
-  // whole tiles.
-  const int64_t tiles_per_cu = (p->ntiles * p->S + cus - 1) / cus;
-  int nws = 1;
-  if (p->S > 1 || tiles_per_cu < 2 * kNW)
-    while (nws * 2 <= kNW && nws * 2 <= last_seg) nws *= 2;
-  p->NWS = nws;
-  p->NWT = kNW / nws;
+  p->NWS = 0;  // (waves split each workgroup's items evenly)
+  p->NWT = 0;
   p->TB = 1;
-  int64_t P = (p->ntiles + p->NWT - 1) / p->NWT;
+  int64_t P = p->ntiles;
   const int64_t cap = cus / p->S > 0 ? cus / p->S : 1;
   if (P > cap) P = cap;
   p->P = (int)P;
-  p->nb = (int)((p->ntiles + P * p->NWT - 1) / (P * p->NWT));  // tiles per wave
+  p->nb = (int)((p->ntiles + P - 1) / P);  // tiles per workgroup (at most)
   p->wgs = (int64_t)p->S * P;
-  p->red_bytes = (nws > 1 || p->S > 1) ? (size_t)kNW * p->nb * nmat * 512 : 0;
+  p->red_bytes = (size_t)kNW * 2 * nmat * 512;
   p->lds_bytes = (size_t)p->KSP * kSpanLds + p->red_bytes + (size_t)kNW * nmat * kScrDwords * 4;
   if (p->lds_bytes > 160 * 1024 - 64) {
     *why = "LDS budget exceeded";
