@@ -12,14 +12,14 @@
 // activations, and that product runs on v_mfma_scale_f32_16x16x128_f8f6f4:
 //
 // * B operand: the bits of one packed word per lane, expanded to fp4 (E2M1)
-//   codes with four bit-masks (no shifts):
-//     w & 0x11111111 -> nibble = bit 4i   -> code 0.5 * bit
-//     w & 0x22222222 -> nibble = bit 4i+1 -> code 1.0 * bit
-//     w & 0x44444444 -> nibble = bit 4i+2 -> code 2.0 * bit
-//     (w & 0x88888888) | 0x22222222 -> bit 4i+3 -> code 1 - 2*bit
-//   The matching activation (A operand) is scaled by 2, 1, 1/2, -1/2, so each
-//   product is bit*x, except the last class, which adds -x/2; the MFMA's
-//   accumulator input cancels that (and adds -X/2 for symmetric tensors).
+//   codes 1 - 2*bit (+1 for a clear bit, -1 for a set one): for bit class j
+//   (bits 4i+j) the bit is shifted to the code's sign position and OR-ed with
+//   the code of 1.0: ((w << (3-j)) & 0x88888888) | 0x22222222.  Each MFMA
+//   therefore computes D = sum_k (1 - 2 bit_k) x_k = X - 2S, and
+//     symmetric: sum w x = -(s/2) D,
+//     affine:    sum w x = -(s/2) D + (s/2 + b) X,
+//   so the kernel accumulates s*D (and -(s + 2b)*X for affine tensors) and
+//   multiplies by -1/2 at the end.
 // * A operand: each activation as two fp8 (E4M3) pieces, x = hi + lo/16, with
 //   one power-of-two block scale per 32 weights chosen from the block's
 //   largest |x|.  A bf16 value has 8 significant bits, hi carries the top 4
@@ -70,13 +70,13 @@ constexpr int kThreads = kNW * 64;
 constexpr int kKspMax = 14;  // spans per K segment (LDS image 126 KB at most)
 
 // LDS image of one span (4 groups): A operand [g4][half][64 lanes][16 B],
-// block scales [64 lanes][4 groups] bytes, accumulator inputs and group sums
-// [g4][16 D rows] floats (rows 8..15, the lo half, and rows of activation
-// index >= M hold zeros; inactive A rows hold zero bytes and unit scales).
+// block scales [64 lanes][4 groups] bytes, and (affine tensors) the group sums
+// of the activations [g4][16 D rows] floats (rows 8..15, the lo half, and rows
+// of activation index >= M hold zeros; inactive A rows hold zero bytes and
+// unit scales).
 constexpr int kSpanA = 8192;
 constexpr int kOffSc = kSpanA;
-constexpr int kOffCorr = kOffSc + 256;
-constexpr int kOffXs = kOffCorr + 256;
+constexpr int kOffXs = kOffSc + 256;
 constexpr int kSpanLds = kOffXs + 256;
 
 // per-wave LDS scratch of the word transpose: 16 rows x 34 dwords (32 used)
@@ -143,12 +143,9 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
   for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // scale dwords, one per lane
     if (((idx & 15) & 7) >= a.M) reinterpret_cast<uint32_t*>(lds + (idx >> 6) * kSpanLds + kOffSc)[idx & 63] = 0x7f7f7f7fu;
   }
-  for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // [g4][16] sums
-    const int r = idx & 15;
-    if (r >= a.M) {
-      float* base = reinterpret_cast<float*>(lds + (idx >> 6) * kSpanLds);
-      base[kOffCorr / 4 + (idx & 63)] = 0.0f;
-      base[kOffXs / 4 + (idx & 63)] = 0.0f;
+  if (AFFINE) {
+    for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // [g4][16] sums
+      if ((idx & 15) >= a.M) reinterpret_cast<float*>(lds + (idx >> 6) * kSpanLds + kOffXs)[idx & 63] = 0.0f;
     }
   }
   const int items = a.M * nsp * 32;
@@ -168,20 +165,20 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
       xv[2 * d] = __uint_as_float(wd << 16);
       xv[2 * d + 1] = __uint_as_float(wd & 0xffff0000u);
     }
-    // element t has bit position 16*hh + t in the word: class t % 4
-    float cm[4];
+    // block scale from the word's largest |x| (the other half word is the
+    // neighbouring lane)
+    float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      cm[j] = fmaxf(fmaxf(fabsf(xv[j]), fabsf(xv[j + 4])), fmaxf(fabsf(xv[j + 8]), fabsf(xv[j + 12])));
-    float amax = fmaxf(fmaxf(2.0f * cm[0], cm[1]), 0.5f * fmaxf(cm[2], cm[3]));
-    amax = fmaxf(amax, dpp_xor1(amax));  // the word's other half
+    for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(xv[t]));
+    amax = fmaxf(amax, dpp_xor1(amax));
     int sc = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 8 : 0;
     sc = sc < -123 ? -123 : (sc > 127 ? 127 : sc);
-    const float alpha[4] = {2.0f, 1.0f, 0.5f, -0.5f};
+    const float f = ldexpf(1.0f, -sc);
+    // element t has bit position 16*hh + t in the word: class j = t % 4 goes
+    // to A bytes 4 apart (see the byte map below)
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float f = ldexpf(alpha[j], -sc);
       const float v0 = xv[j] * f, v1 = xv[j + 4] * f, v2 = xv[j + 8] * f, v3 = xv[j + 12] * f;
       int h = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
       h = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, h, true);
@@ -195,16 +192,14 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
       lo[j] = (uint32_t)l;
     }
     float X = 0.0f;
+    if (AFFINE) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) X += xv[t];
-    float X3 = (xv[3] + xv[7]) + (xv[11] + xv[15]);
-    // sums over the group's 8 items (4 words x 2 halves)
-    X += dpp_xor1(X);
-    X3 += dpp_xor1(X3);
-    X += dpp_xor2(X);
-    X3 += dpp_xor2(X3);
-    X += dpp_half_mirror(X);
-    X3 += dpp_half_mirror(X3);
+      for (int t = 0; t < 16; ++t) X += xv[t];
+      // sum over the group's 8 items (4 words x 2 halves)
+      X += dpp_xor1(X);
+      X += dpp_xor2(X);
+      X += dpp_half_mirror(X);
+    }
     if (valid) {
       unsigned char* base = lds + sp * kSpanLds;
       const int h2 = b >> 1;
@@ -220,10 +215,7 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
         base[kOffSc + (m + 16 * b) * 4 + g4] = (unsigned char)(sc + 127);
         base[kOffSc + (8 + m + 16 * b) * 4 + g4] = (unsigned char)(sc + 123);
       }
-      if ((it & 7) == 0) {
-        reinterpret_cast<float*>(base + kOffCorr)[g4 * 16 + m] = AFFINE ? 0.5f * X3 : 0.5f * (X3 - X);
-        reinterpret_cast<float*>(base + kOffXs)[g4 * 16 + m] = X;
-      }
+      if (AFFINE && (it & 7) == 0) reinterpret_cast<float*>(base + kOffXs)[g4 * 16 + m] = X;
     }
   }
 }
@@ -402,41 +394,42 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
       const unsigned char* base = lds + (2 * d + half) * kSpanLds;
       const uint32_t scale_a = reinterpret_cast<const uint32_t*>(base + kOffSc)[lane];
       v8i A[4];
-      v4f C[4], XS[4];
+      v4f XS[4];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const u32x4 h0 = reinterpret_cast<const u32x4*>(base + (g4 * 8) * 256)[lane];
         const u32x4 h1 = reinterpret_cast<const u32x4*>(base + (g4 * 8 + 4) * 256)[lane];
         A[g4] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-        C[g4] = reinterpret_cast<const v4f*>(base + kOffCorr)[g4 * 4 + q];
         if (AFFINE) XS[g4] = reinterpret_cast<const v4f*>(base + kOffXs)[g4 * 4 + q];
       }
+      const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt) {
         v4f Dg[4];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const uint32_t wd = bw[mt][4 * half + g4];
-          const v8i B = {(int)(wd & 0x11111111u), (int)(wd & 0x22222222u), (int)(wd & 0x44444444u),
-                         (int)((wd & 0x88888888u) | 0x22222222u), 0, 0, 0, 0};
+          const v8i B = {(int)(((wd << 3) & 0x88888888u) | 0x22222222u), (int)(((wd << 2) & 0x88888888u) | 0x22222222u),
+                         (int)(((wd << 1) & 0x88888888u) | 0x22222222u), (int)((wd & 0x88888888u) | 0x22222222u),
+                         0, 0, 0, 0};
           if (g4 == 0)
-            Dg[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, C[0], 0, 4, 0, (int)scale_a, 0, 0x7f7f7f7f);
+            Dg[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, zero, 0, 4, 0, (int)scale_a, 0, 0x7f7f7f7f);
           else if (g4 == 1)
-            Dg[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, C[1], 0, 4, 1, (int)scale_a, 0, 0x7f7f7f7f);
+            Dg[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, zero, 0, 4, 1, (int)scale_a, 0, 0x7f7f7f7f);
           else if (g4 == 2)
-            Dg[2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, C[2], 0, 4, 2, (int)scale_a, 0, 0x7f7f7f7f);
+            Dg[2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, zero, 0, 4, 2, (int)scale_a, 0, 0x7f7f7f7f);
           else
-            Dg[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[3], B, C[3], 0, 4, 3, (int)scale_a, 0, 0x7f7f7f7f);
+            Dg[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[3], B, zero, 0, 4, 3, (int)scale_a, 0, 0x7f7f7f7f);
         }
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const float sv = meta_at<MBF16, SC128>(sreg[u][mt], 4 * half + g4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(sv, Dg[g4][i], acc[mt][i]);
-          if (AFFINE) {
-            const float bv = meta_at<MBF16, SC128>(breg[u][mt], 4 * half + g4);
+          if (AFFINE) {  // -(s + 2b) X
+            const float cv = -fmaf(2.0f, meta_at<MBF16, SC128>(breg[u][mt], 4 * half + g4), sv);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(bv, XS[g4][i], acc[mt][i]);
+            for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(cv, XS[g4][i], acc[mt][i]);
           }
         }
       }
@@ -472,8 +465,8 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
                                                   false);
       auto p23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[mt][2]), __float_as_uint(acc[mt][3]), false,
                                                   false);
-      comb[mt][0] = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
-      comb[mt][1] = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
+      comb[mt][0] = -0.5f * (__uint_as_float(p01[0]) + __uint_as_float(p01[1]));
+      comb[mt][1] = -0.5f * (__uint_as_float(p23[0]) + __uint_as_float(p23[1]));
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0f;
     }
