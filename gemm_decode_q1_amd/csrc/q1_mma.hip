@@ -12,20 +12,21 @@
 // activations, and that product runs on v_mfma_scale_f32_16x16x128_f8f6f4:
 //
 // * B operand: the bits of one packed word per lane, expanded to fp4 (E2M1)
-//   codes 1 - 2*bit (+1 for a clear bit, -1 for a set one): for bit class j
-//   (bits 4i+j) the bit is shifted to the code's sign position and OR-ed with
-//   the code of 1.0: ((w << (3-j)) & 0x88888888) | 0x22222222.  Each MFMA
-//   therefore computes D = sum_k (1 - 2 bit_k) x_k = X - 2S, and
-//     symmetric: sum w x = -(s/2) D,
-//     affine:    sum w x = -(s/2) D + (s/2 + b) X,
-//   so the kernel accumulates s*D (and -(s + 2b)*X for affine tensors) and
-//   multiplies by -1/2 at the end.
+//   codes by bit class j (bits 4i+j of the word, nibble i): classes 0, 1, 2
+//   keep their bit in place (codes 0.5, 1 and 2 for a set bit, 0 for a clear
+//   one: one AND each) and class 3 moves its bit to position 2 (code 2).  The
+//   activations of class j are pre-multiplied by 1/code (2, 1, 1/2, 1/2, all
+//   powers of two, so exact), which makes each MFMA compute
+//   D = S = sum of x over the set bits of the group.  Then
+//     symmetric: sum w x = s (S - X/2),  affine: sum w x = s S + b X,
+//   with X the group sum of x: for symmetric tensors -X/2 enters as the
+//   MFMA's accumulator input, for affine ones b X is added after it.
 // * A operand: each activation as two fp8 (E4M3) pieces, x = hi + lo/16, with
 //   one power-of-two block scale per 32 weights chosen from the block's
 //   largest |x|.  A bf16 value has 8 significant bits, hi carries the top 4
-//   and lo the rest, so the pair is exact for every element within 2^14 of
-//   its block's largest magnitude; below that the error is at most 2^-21 of
-//   the block maximum.  Rows 0..7 of the 16-row A tile hold hi for the M
+//   (rounded) and lo the rest, so the pair is exact for every element within
+//   2^12 of its block's largest magnitude; below that the error is at most
+//   2^-19 of the block maximum.  Rows 0..7 of the 16-row A tile hold hi for the M
 //   activation rows and rows 8..15 hold lo; the two halves of the result are
 //   added at the end.
 // * One instruction covers 16 weight rows x one group (128 weights): its fp32
@@ -64,20 +65,28 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kNW = 8;  // waves per workgroup
 constexpr int kThreads = kNW * 64;
 constexpr int kKspMax = 14;  // spans per K segment (LDS image 126 KB at most)
 
 // LDS image of one span (4 groups): A operand [g4][half][64 lanes][16 B],
-// block scales [64 lanes][4 groups] bytes, and (affine tensors) the group sums
-// of the activations [g4][16 D rows] floats (rows 8..15, the lo half, and rows
+// block scales [64 lanes][4 groups] bytes, and the group sums of the
+// activations [g4][16 D rows] floats (-X/2 for symmetric tensors, X for affine) (rows 8..15, the lo half, and rows
 // of activation index >= M hold zeros; inactive A rows hold zero bytes and
-// unit scales).
+// unit scales).  Within each 1 KB block (g4, half) the 16-byte chunk of lane
+// 16*qa + row is stored at position 16*qa + (row ^ a_swz(qa, block)): reads of
+// 8 (or 16) consecutive lanes still cover distinct banks, and the conversion,
+// whose 8 neighbouring lanes write one activation row of 8 (qa, half) pairs
+// (16 with the next g4), spreads its writes over the banks too.
 constexpr int kSpanA = 8192;
 constexpr int kOffSc = kSpanA;
 constexpr int kOffXs = kOffSc + 256;
 constexpr int kSpanLds = kOffXs + 256;
+
+__device__ __forceinline__ int a_swz(int qa, int blk) { return qa | ((blk & 3) << 2); }
 
 // per-wave LDS scratch of the word transpose: 16 rows x 34 dwords (32 used)
 constexpr int kScrStride = 34;
@@ -98,6 +107,10 @@ __device__ __forceinline__ float dpp_xor2(float v) {  // quad_perm [2,3,0,1]
 }
 __device__ __forceinline__ float dpp_half_mirror(float v) {  // lane i <- lane 7-i within 8
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ uint32_t dpp_xor1_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false);
 }
 
 // Conversion of the activations of spans [span0, span0 + nsp) into the LDS
@@ -134,7 +147,7 @@ template <bool AFFINE>
 __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int tid, const PrepLoads& L) {
   // rows no item writes: inactive A rows, their scales, lo/inactive sums
   for (int idx = tid; idx < nsp * 512; idx += kThreads) {  // 16-byte A chunks
-    const int mrow = idx & 15;
+    const int mrow = (idx & 15) ^ a_swz((idx >> 4) & 3, (idx >> 6) & 7);
     if ((mrow & 7) >= a.M) {
       const u32x4 z = {0u, 0u, 0u, 0u};
       reinterpret_cast<u32x4*>(lds + (idx >> 9) * kSpanLds)[idx & 511] = z;
@@ -143,10 +156,8 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
   for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // scale dwords, one per lane
     if (((idx & 15) & 7) >= a.M) reinterpret_cast<uint32_t*>(lds + (idx >> 6) * kSpanLds + kOffSc)[idx & 63] = 0x7f7f7f7fu;
   }
-  if (AFFINE) {
-    for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // [g4][16] sums
-      if ((idx & 15) >= a.M) reinterpret_cast<float*>(lds + (idx >> 6) * kSpanLds + kOffXs)[idx & 63] = 0.0f;
-    }
+  for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // [g4][16] sums
+    if ((idx & 15) >= a.M) reinterpret_cast<float*>(lds + (idx >> 6) * kSpanLds + kOffXs)[idx & 63] = 0.0f;
   }
   const int items = a.M * nsp * 32;
 #pragma unroll
@@ -171,51 +182,59 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
 #pragma unroll
     for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(xv[t]));
     amax = fmaxf(amax, dpp_xor1(amax));
-    int sc = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 8 : 0;
-    sc = sc < -123 ? -123 : (sc > 127 ? 127 : sc);
-    const float f = ldexpf(1.0f, -sc);
+    // |x| * 2^-sc < 2^7, at most 2^8 after the class factor: below the
+    // largest fp8 value, 448.  The clamp keeps every divisor below a normal
+    // fp32 power of two (bf16 data never reaches it at the top).
+    int sc = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 7 : 0;
+    sc = sc < -118 ? -118 : (sc > 125 ? 125 : sc);
     // element t has bit position 16*hh + t in the word: class j = t % 4 goes
-    // to A bytes 4 apart (see the byte map below)
+    // to A bytes 4 apart (see the byte map below), times 1/code(j).  The
+    // scaled conversions divide by (and the decode multiplies by) a power of
+    // two: 2^sc / factor(j) for hi, 16 times less for lo.
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float v0 = xv[j] * f, v1 = xv[j + 4] * f, v2 = xv[j + 8] * f, v3 = xv[j + 12] * f;
-      int h = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
-      h = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, h, true);
-      const float r0 = (v0 - __builtin_amdgcn_cvt_f32_fp8(h, 0)) * 16.0f;
-      const float r1 = (v1 - __builtin_amdgcn_cvt_f32_fp8(h, 1)) * 16.0f;
-      const float r2 = (v2 - __builtin_amdgcn_cvt_f32_fp8(h, 2)) * 16.0f;
-      const float r3 = (v3 - __builtin_amdgcn_cvt_f32_fp8(h, 3)) * 16.0f;
-      int l = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
-      l = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, l, true);
-      hi[j] = (uint32_t)h;
-      lo[j] = (uint32_t)l;
+      const int e = sc - (j == 0 ? 1 : (j == 1 ? 0 : -1));  // 2^e = 2^sc / factor(j)
+      const float dh = __uint_as_float((uint32_t)(e + 127) << 23);
+      const float dl = __uint_as_float((uint32_t)(e + 123) << 23);
+      v2s h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, xv[j], xv[j + 4], dh, false);
+      h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, xv[j + 8], xv[j + 12], dh, true);
+      const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+      const v2f d01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb, dh, false);
+      const v2f d23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb, dh, true);
+      v2s l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, xv[j] - d01[0], xv[j + 4] - d01[1], dl, false);
+      l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, xv[j + 8] - d23[0], xv[j + 12] - d23[1], dl, true);
+      hi[j] = hb;
+      lo[j] = __builtin_bit_cast(uint32_t, l);
     }
     float X = 0.0f;
-    if (AFFINE) {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) X += xv[t];
-      // sum over the group's 8 items (4 words x 2 halves)
-      X += dpp_xor1(X);
-      X += dpp_xor2(X);
-      X += dpp_half_mirror(X);
-    }
+    for (int t = 0; t < 16; ++t) X += xv[t];
+    // sum over the group's 8 items (4 words x 2 halves)
+    X += dpp_xor1(X);
+    X += dpp_xor2(X);
+    X += dpp_half_mirror(X);
+    // A chunk (row, quarter qa, half h2) holds dword 2*(j & 1) + hh = the
+    // class-j bytes of half word hh, for the two classes j with j >> 1 ==
+    // qa & 1, where qa = 2*(b & 1) + (j >> 1) and h2 = b >> 1.  This lane
+    // (hh) writes the chunk of classes 2*hh, 2*hh + 1 and gets the other
+    // half word's bytes of those classes from its neighbour.
+    const uint32_t sh0 = hh ? hi[0] : hi[2], sh1 = hh ? hi[1] : hi[3];
+    const uint32_t sl0 = hh ? lo[0] : lo[2], sl1 = hh ? lo[1] : lo[3];
+    const uint32_t rh0 = dpp_xor1_u(sh0), rh1 = dpp_xor1_u(sh1), rl0 = dpp_xor1_u(sl0), rl1 = dpp_xor1_u(sl1);
+    const u32x4 ch = hh ? u32x4{rh0, hi[2], rh1, hi[3]} : u32x4{hi[0], rh0, hi[1], rh1};
+    const u32x4 cl = hh ? u32x4{rl0, lo[2], rl1, lo[3]} : u32x4{lo[0], rl0, lo[1], rl1};
     if (valid) {
       unsigned char* base = lds + sp * kSpanLds;
-      const int h2 = b >> 1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int qa = 2 * (b & 1) + (j >> 1);
-        const int dw = 2 * (j & 1) + hh;
-        uint32_t* dst = reinterpret_cast<uint32_t*>(base + (g4 * 8 + h2 * 4 + qa) * 256 + m * 16 + dw * 4);
-        dst[0] = hi[j];
-        dst[32] = lo[j];  // row 8 + m: 8 rows * 16 B further
-      }
+      const int h2 = b >> 1, qa = 2 * (b & 1) + hh, blk = 2 * g4 + h2, sw = a_swz(qa, blk);
+      u32x4* blkp = reinterpret_cast<u32x4*>(base) + blk * 64 + qa * 16;
+      blkp[m ^ sw] = ch;
+      blkp[(8 + m) ^ sw] = cl;
       if (hh == 0) {
         base[kOffSc + (m + 16 * b) * 4 + g4] = (unsigned char)(sc + 127);
         base[kOffSc + (8 + m + 16 * b) * 4 + g4] = (unsigned char)(sc + 123);
       }
-      if (AFFINE && (it & 7) == 0) reinterpret_cast<float*>(base + kOffXs)[g4 * 16 + m] = X;
+      if ((it & 7) == 0) reinterpret_cast<float*>(base + kOffXs)[g4 * 16 + m] = AFFINE ? X : -0.5f * X;
     }
   }
 }
@@ -321,6 +340,7 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   const int q = lane >> 4;    // lane quarter
   const int lr = lane >> 3;   // row within a load instruction
   const int lc = lane & 7;    // 16-byte chunk (group) within a row's 128 bytes
+  const int lane_sw = lane ^ q;  // A chunk position of this lane, before the block's part of the swizzle
   const uint32_t row_bytes = (uint32_t)a.K >> 3;
   // row indices fit in 31 bits (the plan keeps N*K/8 below 2^31)
   const int Nrows = (int)a.N;
@@ -397,10 +417,10 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
       v4f XS[4];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const u32x4 h0 = reinterpret_cast<const u32x4*>(base + (g4 * 8) * 256)[lane];
-        const u32x4 h1 = reinterpret_cast<const u32x4*>(base + (g4 * 8 + 4) * 256)[lane];
+        const u32x4 h0 = reinterpret_cast<const u32x4*>(base + (g4 * 8) * 256)[lane_sw ^ ((g4 & 1) << 3)];
+        const u32x4 h1 = reinterpret_cast<const u32x4*>(base + (g4 * 8 + 4) * 256)[lane_sw ^ (4 | ((g4 & 1) << 3))];
         A[g4] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-        if (AFFINE) XS[g4] = reinterpret_cast<const v4f*>(base + kOffXs)[g4 * 4 + q];
+        XS[g4] = reinterpret_cast<const v4f*>(base + kOffXs)[g4 * 4 + q];
       }
       const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -409,27 +429,27 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const uint32_t wd = bw[mt][4 * half + g4];
-          const v8i B = {(int)(((wd << 3) & 0x88888888u) | 0x22222222u), (int)(((wd << 2) & 0x88888888u) | 0x22222222u),
-                         (int)(((wd << 1) & 0x88888888u) | 0x22222222u), (int)((wd & 0x88888888u) | 0x22222222u),
-                         0, 0, 0, 0};
+          const v8i B = {(int)(wd & 0x11111111u), (int)(wd & 0x22222222u), (int)(wd & 0x44444444u),
+                         (int)((wd >> 1) & 0x44444444u), 0, 0, 0, 0};
+          const v4f C = AFFINE ? zero : XS[g4];
           if (g4 == 0)
-            Dg[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, zero, 0, 4, 0, (int)scale_a, 0, 0x7f7f7f7f);
+            Dg[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, C, 0, 4, 0, (int)scale_a, 0, 0x7f7f7f7f);
           else if (g4 == 1)
-            Dg[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, zero, 0, 4, 1, (int)scale_a, 0, 0x7f7f7f7f);
+            Dg[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, C, 0, 4, 1, (int)scale_a, 0, 0x7f7f7f7f);
           else if (g4 == 2)
-            Dg[2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, zero, 0, 4, 2, (int)scale_a, 0, 0x7f7f7f7f);
+            Dg[2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, C, 0, 4, 2, (int)scale_a, 0, 0x7f7f7f7f);
           else
-            Dg[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[3], B, zero, 0, 4, 3, (int)scale_a, 0, 0x7f7f7f7f);
+            Dg[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[3], B, C, 0, 4, 3, (int)scale_a, 0, 0x7f7f7f7f);
         }
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const float sv = meta_at<MBF16, SC128>(sreg[u][mt], 4 * half + g4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(sv, Dg[g4][i], acc[mt][i]);
-          if (AFFINE) {  // -(s + 2b) X
-            const float cv = -fmaf(2.0f, meta_at<MBF16, SC128>(breg[u][mt], 4 * half + g4), sv);
+          if (AFFINE) {  // + b X
+            const float bv = meta_at<MBF16, SC128>(breg[u][mt], 4 * half + g4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(cv, XS[g4][i], acc[mt][i]);
+            for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(bv, XS[g4][i], acc[mt][i]);
           }
         }
       }
@@ -465,8 +485,8 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
                                                   false);
       auto p23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[mt][2]), __float_as_uint(acc[mt][3]), false,
                                                   false);
-      comb[mt][0] = -0.5f * (__uint_as_float(p01[0]) + __uint_as_float(p01[1]));
-      comb[mt][1] = -0.5f * (__uint_as_float(p23[0]) + __uint_as_float(p23[1]));
+      comb[mt][0] = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
+      comb[mt][1] = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0f;
     }
@@ -495,9 +515,9 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
     }
   };
 
-  // Whole turns of the ring (items past the end load nothing and add zeros
-  // and end no tile): a loop body without early exits keeps the ring in place
-  // across iterations.
+  // Whole turns of the ring (slots past the end load nothing, compute
+  // nothing and end no tile): a loop body without early exits keeps the ring
+  // in place across iterations.
   const int nitems_pad = (nitems + D - 1) / D * D;
   int k = kfirst, d = i0 - kfirst * nds;  // current item
   int ik = k, id = d + D;                 // item + D (next loads)
@@ -508,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   for (int base = 0; base < nitems_pad; base += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      compute(u, d);
+      if (base + u < nitems) compute(u, d);  // (uniform) the last turn's empty slots do no work
       issue(u, ik, id, base + u + D < nitems);
       __builtin_amdgcn_sched_barrier(0);  // keep items apart: bounded register use
       if (base + u < nitems && (d == nds - 1 || base + u == nitems - 1)) tile_done(k);
