@@ -67,6 +67,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short v2s __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kNW = 8;  // waves per workgroup
 constexpr int kThreads = kNW * 64;
@@ -74,18 +75,20 @@ constexpr int kKspMax = 14;  // spans per K segment (LDS image 126 KB at most)
 
 // LDS image of one span (4 groups): A operand [g4][half][64 lanes][16 B],
 // block scales [64 lanes][4 groups] bytes, and the group sums of the
-// activations [g4][16 D rows] floats (-X/2 for symmetric tensors, X for affine) (rows 8..15, the lo half, and rows
-// of activation index >= M hold zeros; inactive A rows hold zero bytes and
-// unit scales).  Within each 1 KB block (g4, half) the 16-byte chunk of lane
-// 16*qa + row is stored at position 16*qa + (row ^ a_swz(qa, block)): reads of
-// 8 (or 16) consecutive lanes still cover distinct banks, and the conversion,
-// whose 8 neighbouring lanes write one activation row of 8 (qa, half) pairs
-// (16 with the next g4), spreads its writes over the banks too.
-constexpr int kSpanA = 8192;
+// activations [g4][16 D rows] floats (-X/2 for symmetric tensors, X for affine)
+// (rows 8..15, the lo half, and rows of activation index >= M hold zeros;
+// inactive A rows hold zero bytes and unit scales).  Within each 1 KB block
+// (g4, half) the 16-byte chunk of lane 16*qa + row is stored at position
+// 16*qa + (row ^ a_swz(qa, block)), and the blocks of group g4 start 16*g4
+// bytes late: reads of 8 (or 16) consecutive lanes still cover distinct
+// banks, and the conversion's dword writes (one activation row, 4 words x 4
+// groups x 2 half words per instruction) spread over the banks too.
+constexpr int kSpanA = 4 * 2064;
 constexpr int kOffSc = kSpanA;
 constexpr int kOffXs = kOffSc + 256;
 constexpr int kSpanLds = kOffXs + 256;
 
+__device__ __forceinline__ int a_blk_off(int blk) { return blk * 1024 + (blk >> 1) * 16; }
 __device__ __forceinline__ int a_swz(int qa, int blk) { return qa | ((blk & 3) << 2); }
 
 // per-wave LDS scratch of the word transpose: 16 rows x 34 dwords (32 used)
@@ -109,9 +112,6 @@ __device__ __forceinline__ float dpp_half_mirror(float v) {  // lane i <- lane 7
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ uint32_t dpp_xor1_u(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false);
-}
 
 // Conversion of the activations of spans [span0, span0 + nsp) into the LDS
 // image.  Item = (row m, span, word, half word): 16 activations, one dword of
@@ -127,13 +127,14 @@ struct PrepLoads {
 __device__ __forceinline__ void prep_load(const MmaArgs& a, int span0, int nsp, int tid, PrepLoads& L) {
   const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, a.x_bytes);
   const int items = a.M * nsp * 32;
+  const float inv_nsp = 1.0f / (float)nsp;
 #pragma unroll
   for (int r = 0; r < kPrepRounds; ++r) {
     const int it = tid + r * kThreads;
     const bool valid = it < items;
     const int hh = it & 1, wi = (it >> 1) & 15, ms = it >> 5;
-    const int m = valid ? ms / nsp : 0;
-    const int sp = valid ? ms - m * nsp : 0;
+    const int m = (int)(((float)ms + 0.5f) * inv_nsp);  // ms / nsp (exact: ms < 8 * kKspMax)
+    const int sp = ms - m * nsp;
     const int k0 = (span0 + sp) * 512 + wi * 32 + hh * 16;
     const uint32_t off = (uint32_t)(((int64_t)m * a.x_ld + k0) * 2) | ((valid && k0 < a.K) ? 0u : kOOB);
     if (r * kThreads < items) {  // uniform: skip rounds nobody needs
@@ -147,10 +148,11 @@ template <bool AFFINE>
 __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int tid, const PrepLoads& L) {
   // rows no item writes: inactive A rows, their scales, lo/inactive sums
   for (int idx = tid; idx < nsp * 512; idx += kThreads) {  // 16-byte A chunks
-    const int mrow = (idx & 15) ^ a_swz((idx >> 4) & 3, (idx >> 6) & 7);
+    const int c = idx & 511, blk = c >> 6, pos = c & 63;
+    const int mrow = (pos & 15) ^ a_swz(pos >> 4, blk);
     if ((mrow & 7) >= a.M) {
       const u32x4 z = {0u, 0u, 0u, 0u};
-      reinterpret_cast<u32x4*>(lds + (idx >> 9) * kSpanLds)[idx & 511] = z;
+      *reinterpret_cast<u32x4*>(lds + (idx >> 9) * kSpanLds + a_blk_off(blk) + pos * 16) = z;
     }
   }
   for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // scale dwords, one per lane
@@ -160,15 +162,21 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
     if ((idx & 15) >= a.M) reinterpret_cast<float*>(lds + (idx >> 6) * kSpanLds + kOffXs)[idx & 63] = 0.0f;
   }
   const int items = a.M * nsp * 32;
+  // item = tid + 512 r: half word hh and word wi do not depend on the round;
+  // (row, span) index ms = tid/32 + 16 r is split by a rounded reciprocal
+  // (ms < 8 * kKspMax keeps it exact)
+  const int hh = tid & 1, wi = (tid >> 1) & 15;
+  const int g4 = wi >> 2, b = wi & 3;
+  const float inv_nsp = 1.0f / (float)nsp;
+  const v2bf ones = __builtin_bit_cast(v2bf, 0x3F803F80u);
 #pragma unroll
   for (int r = 0; r < kPrepRounds; ++r) {
     if (r * kThreads >= items) break;  // uniform; rounds with items keep whole waves (items % 64 == 0)
     const int it = tid + r * kThreads;
     const bool valid = it < items;
-    const int hh = it & 1, wi = (it >> 1) & 15, ms = it >> 5;
-    const int m = valid ? ms / nsp : 0;
-    const int sp = valid ? ms - m * nsp : 0;
-    const int g4 = wi >> 2, b = wi & 3;
+    const int ms = it >> 5;
+    const int m = (int)(((float)ms + 0.5f) * inv_nsp);
+    const int sp = ms - m * nsp;
     float xv[16];
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
@@ -209,27 +217,27 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
     }
     float X = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) X += xv[t];
+    for (int d = 0; d < 8; ++d)
+      X = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, d < 4 ? L.q[r][0][d] : L.q[r][1][d - 4]), ones,
+                                          X, false);
     // sum over the group's 8 items (4 words x 2 halves)
     X += dpp_xor1(X);
     X += dpp_xor2(X);
     X += dpp_half_mirror(X);
-    // A chunk (row, quarter qa, half h2) holds dword 2*(j & 1) + hh = the
-    // class-j bytes of half word hh, for the two classes j with j >> 1 ==
-    // qa & 1, where qa = 2*(b & 1) + (j >> 1) and h2 = b >> 1.  This lane
-    // (hh) writes the chunk of classes 2*hh, 2*hh + 1 and gets the other
-    // half word's bytes of those classes from its neighbour.
-    const uint32_t sh0 = hh ? hi[0] : hi[2], sh1 = hh ? hi[1] : hi[3];
-    const uint32_t sl0 = hh ? lo[0] : lo[2], sl1 = hh ? lo[1] : lo[3];
-    const uint32_t rh0 = dpp_xor1_u(sh0), rh1 = dpp_xor1_u(sh1), rl0 = dpp_xor1_u(sl0), rl1 = dpp_xor1_u(sl1);
-    const u32x4 ch = hh ? u32x4{rh0, hi[2], rh1, hi[3]} : u32x4{hi[0], rh0, hi[1], rh1};
-    const u32x4 cl = hh ? u32x4{rl0, lo[2], rl1, lo[3]} : u32x4{lo[0], rl0, lo[1], rl1};
     if (valid) {
+      // A chunk (row, quarter qa, block (g4, h2)) holds in dword 2*(j & 1) +
+      // hh the class-j bytes of half word hh, where qa = 2*(b & 1) + (j >> 1)
+      // and h2 = b >> 1
       unsigned char* base = lds + sp * kSpanLds;
-      const int h2 = b >> 1, qa = 2 * (b & 1) + hh, blk = 2 * g4 + h2, sw = a_swz(qa, blk);
-      u32x4* blkp = reinterpret_cast<u32x4*>(base) + blk * 64 + qa * 16;
-      blkp[m ^ sw] = ch;
-      blkp[(8 + m) ^ sw] = cl;
+      const int blk = 2 * g4 + (b >> 1);
+      unsigned char* bb = base + a_blk_off(blk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int qa = 2 * (b & 1) + (j >> 1), sw = a_swz(qa, blk);
+        const int dw = 2 * (j & 1) + hh;
+        *reinterpret_cast<uint32_t*>(bb + (qa * 16 + (m ^ sw)) * 16 + dw * 4) = hi[j];
+        *reinterpret_cast<uint32_t*>(bb + (qa * 16 + ((8 + m) ^ sw)) * 16 + dw * 4) = lo[j];
+      }
       if (hh == 0) {
         base[kOffSc + (m + 16 * b) * 4 + g4] = (unsigned char)(sc + 127);
         base[kOffSc + (8 + m + 16 * b) * 4 + g4] = (unsigned char)(sc + 123);
@@ -417,8 +425,8 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
       v4f XS[4];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const u32x4 h0 = reinterpret_cast<const u32x4*>(base + (g4 * 8) * 256)[lane_sw ^ ((g4 & 1) << 3)];
-        const u32x4 h1 = reinterpret_cast<const u32x4*>(base + (g4 * 8 + 4) * 256)[lane_sw ^ (4 | ((g4 & 1) << 3))];
+        const u32x4 h0 = reinterpret_cast<const u32x4*>(base + a_blk_off(2 * g4))[lane_sw ^ ((g4 & 1) << 3)];
+        const u32x4 h1 = reinterpret_cast<const u32x4*>(base + a_blk_off(2 * g4 + 1))[lane_sw ^ (4 | ((g4 & 1) << 3))];
         A[g4] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
         XS[g4] = reinterpret_cast<const v4f*>(base + kOffXs)[g4 * 4 + q];
       }
