@@ -95,16 +95,14 @@ struct MmaPlan {
   int64_t ntiles;  // tiles of 16 rows
   int S;           // K segments (grid split); S > 1 finishes in the kernel
   int KSP;         // spans per K segment (the last may have fewer)
-  int NWS, NWT;    // waves splitting a segment's spans x waves splitting its tiles
-  int TB;          // (1)
   int P;           // workgroups per K segment
-  int nb;          // tiles per wave
-  int cgroup;      // S > 1: tiles per arrival counter
-  size_t red_bytes;  // LDS for the cross-wave sums
+  int nb;          // tiles per workgroup (at most)
+  int TW;          // result slots per wave: tiles one wave's items touch (at most)
+  size_t red_bytes;  // LDS for the per-wave tile results
   int64_t wgs;     // S * P
   size_t lds_bytes;
   size_t partial_floats;  // S > 1: S*M*N*(pair ? 2 : 1)
-  size_t counters;        // S > 1: nb * P
+  size_t counters;        // S > 1: P
 };
 
 struct MmaArgs {
@@ -118,7 +116,7 @@ struct MmaArgs {
   const uint16_t* b1;
   int64_t N;
   int32_t M, K, G, nspan;
-  int32_t S, KSP, NWS, NWT, P, nb, cgroup;
+  int32_t S, KSP, P, nb, TW;
   uint32_t red_bytes;
   uint32_t x_bytes, packed_bytes, meta_bytes;
   int32_t out_dtype;

@@ -303,11 +303,13 @@ __device__ __forceinline__ float meta_at(const uint32_t* v, int g) {
 // rows each; consecutive tiles go to different workgroups) and the segment's
 // double spans (8 groups, 128 bytes of every row).  Its items (local tile k,
 // double span d), tiles outer, are split evenly over its 8 waves: wave w takes
-// items [w*I/8, (w+1)*I/8).  A tile that lies inside one wave's range is stored
-// by that wave straight from registers; the (at most two) partial tiles at the
-// ends of each wave's range meet in LDS after the loop and are added in wave
-// order.  Item i of a wave sits in ring slot i % D; its loads are issued D
-// items ahead.
+// items [w*I/8, (w+1)*I/8).  Each wave leaves its sum for every tile its range
+// touches in LDS (slot = tile - its first tile); after the loop the slots of a
+// tile are added in wave order and stored.  The ring loop itself stores
+// nothing to memory: stores there would count in the same counter as the ring's
+// loads and make the waits for each slot's data also wait for newer loads.
+// Item i of a wave sits in ring slot i % D; its loads are issued D items
+// ahead.
 //
 // Loads: instruction h of an item reads rows 8h..8h+7 of the tile, lane l the
 // 16 bytes (group l%8, 4 words) of row l/8, so each row's 128 bytes come from
@@ -393,6 +395,7 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       issue(u, k, d, u < nitems);
+      __builtin_amdgcn_sched_barrier(0);  // slot by slot, in the loop's order (exact waits at the loop head)
       if (++d == nds) {
         d = 0;
         ++k;
@@ -482,44 +485,20 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
 
   // End of this wave's part of local tile k: lane l of half ab holds
   // activation row 4*((l>>4)&1) + 2*ab + (l>>5) of weight row l & 15 (hi + lo
-  // combined).  A whole tile is emitted; a partial one goes to LDS slot
-  // (wave, k == first tile ? 0 : 1).
+  // combined); it goes to LDS slot (wave, k - first tile of the wave).
   const int kfirst = i0 / (nds > 0 ? nds : 1);
   auto tile_done = [&](int k) {
-    float comb[NMAT][2];
 #pragma unroll
     for (int mt = 0; mt < NMAT; ++mt) {
       auto p01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[mt][0]), __float_as_uint(acc[mt][1]), false,
                                                   false);
       auto p23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[mt][2]), __float_as_uint(acc[mt][3]), false,
                                                   false);
-      comb[mt][0] = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
-      comb[mt][1] = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
+      float* slot = red + (((wave * a.TW + (k - kfirst)) * NMAT + mt) * 2) * 64 + lane;
+      slot[0] = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
+      slot[64] = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0f;
-    }
-    const bool whole = k * nds >= i0 && (k + 1) * nds <= i1;
-    if (whole) {
-      const int row = tile_of(k) * 16 + nl;
-      const int mA = 4 * ((lane >> 4) & 1) + (lane >> 5);
-      if (row < Nrows) {
-#pragma unroll
-        for (int ab = 0; ab < 2; ++ab) {
-          const int m = mA + 2 * ab;
-          if (m < a.M) {
-            float v[NMAT];
-#pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt) v[mt] = comb[mt][ab];
-            emit(m, row, v);
-          }
-        }
-      }
-    } else {
-      const int slot = (k == kfirst) ? 0 : 1;
-#pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt)
-#pragma unroll
-        for (int ab = 0; ab < 2; ++ab) red[(((wave * 2 + slot) * NMAT + mt) * 2 + ab) * 64 + lane] = comb[mt][ab];
     }
   };
 
@@ -551,26 +530,26 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
     }
   }
 
-  // ---- partial tiles: contributions of consecutive waves, in wave order ----
+  // ---- tile results: the slots of the waves that touched each tile, in
+  // wave order ----
   lds_barrier();
   for (int o = tid; o < nbp * 128; o += kThreads) {
     const int kk = o >> 7, r = o & 127, ab = r >> 6, l = r & 63;
-    const int t0 = kk * nds, t1 = t0 + nds;  // the tile's items
-    int wa = 0;
-    while (((wa + 1) * I) / kNW <= t0) ++wa;  // wave holding item t0
-    if ((wa * I) / kNW <= t0 && ((wa + 1) * I) / kNW >= t1) continue;  // whole in one wave: emitted
     const int m = 4 * ((l >> 4) & 1) + 2 * ab + (l >> 5);
     const int row = tile_of(kk) * 16 + (l & 15);
     if (m >= a.M || row >= Nrows) continue;
+    const int t0 = kk * nds, t1 = t0 + nds;  // the tile's items
+    int wa = (t0 * kNW) / I;                 // first wave whose range can hold item t0
+    while (((wa + 1) * I) / kNW <= t0) ++wa;
     float v[NMAT];
 #pragma unroll
     for (int mt = 0; mt < NMAT; ++mt) v[mt] = 0.0f;
     for (int w2 = wa; w2 < kNW && (w2 * I) / kNW < t1; ++w2) {
       const int w_i0 = (w2 * I) / kNW;
       if (((w2 + 1) * I) / kNW == w_i0) continue;  // wave without items
-      const int slot = (kk == w_i0 / nds) ? 0 : 1;
 #pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt) v[mt] += red[(((w2 * 2 + slot) * NMAT + mt) * 2 + ab) * 64 + l];
+      for (int mt = 0; mt < NMAT; ++mt)
+        v[mt] += red[(((w2 * a.TW + (kk - w_i0 / nds)) * NMAT + mt) * 2 + ab) * 64 + l];
     }
     emit(m, row, v);
   }
@@ -667,16 +646,29 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, c
   const int kds = (ndsp + p->S - 1) / p->S;
   p->S = (ndsp + kds - 1) / kds;
   p->KSP = 2 * kds;
-  p->NWS = 0;  // (waves split each workgroup's items evenly)
-  p->NWT = 0;
-  p->TB = 1;
   int64_t P = p->ntiles;
   const int64_t cap = cus / p->S > 0 ? cus / p->S : 1;
   if (P > cap) P = cap;
   p->P = (int)P;
   p->nb = (int)((p->ntiles + P - 1) / P);  // tiles per workgroup (at most)
   p->wgs = (int64_t)p->S * P;
-  p->red_bytes = (size_t)kNW * 2 * nmat * 512;
+  {  // most tiles one wave's item range touches, over every workgroup size
+     // (nbp <= nb tiles) and segment length (nds <= kds double spans)
+    int tw = 1;
+    for (int nbp = 1; nbp <= p->nb; ++nbp)
+      for (int nds = 1; nds <= kds; ++nds) {
+        const int64_t I = (int64_t)nbp * nds;
+        for (int w = 0; w < kNW; ++w) {
+          const int64_t i0 = w * I / kNW, i1 = (w + 1) * I / kNW;
+          if (i1 > i0) {
+            const int t = (int)((i1 - 1) / nds - i0 / nds + 1);
+            if (t > tw) tw = t;
+          }
+        }
+      }
+    p->TW = tw;
+  }
+  p->red_bytes = (size_t)kNW * p->TW * nmat * 512;
   p->lds_bytes = (size_t)p->KSP * kSpanLds + p->red_bytes + (size_t)kNW * nmat * kScrDwords * 4;
   if (p->lds_bytes > 160 * 1024 - 64) {
     *why = "LDS budget exceeded";
@@ -686,7 +678,6 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, c
     *why = "activation conversion exceeds its register rounds";
     return false;
   }
-  p->cgroup = 1;
   p->partial_floats = p->S > 1 ? (size_t)p->S * M * N * nmat : 0;
   p->counters = p->S > 1 ? (size_t)P : 0;  // one per workgroup column p (P <= CUs)
   return true;
@@ -710,11 +701,9 @@ hipError_t launch_mma(const MmaPlan& p, const uint16_t* x, int64_t x_ld, const Q
   g.nspan = p.nspan;
   g.S = p.S;
   g.KSP = p.KSP;
-  g.NWS = p.NWS;
-  g.NWT = p.NWT;
   g.P = p.P;
   g.nb = p.nb;
-  g.cgroup = p.cgroup;
+  g.TW = p.TW;
   g.red_bytes = (uint32_t)p.red_bytes;
   g.x_bytes = (uint32_t)(((p.M - 1) * x_ld + a.K) * 2);
   g.packed_bytes = (uint32_t)(a.N * (a.K / 8));
