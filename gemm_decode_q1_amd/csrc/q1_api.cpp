@@ -118,14 +118,15 @@ constexpr size_t kReserved = Q1_WS_RESERVED_BYTES;
 // activation row, the matrix-core kernel (q1_mma.hip) for 2..8 rows, where
 // table lookups grow with the row count.  Q1_PACKED_KERNEL=table|mma forces
 // one of them for every row count.
-bool use_table_kernel(int M) {
+// 0: default routing, 1: table kernel forced, 2: matrix-core kernel forced
+int packed_kernel_env() {
   static const int v = [] {
     const char* e = getenv("Q1_PACKED_KERNEL");
     if (e && strcmp(e, "table") == 0) return 1;
     if (e && strcmp(e, "mma") == 0) return 2;
     return 0;
   }();
-  return v == 1 || (v == 0 && M == 1);
+  return v;
 }
 
 struct PackedPlan {
@@ -135,10 +136,34 @@ struct PackedPlan {
   size_t partial_floats() const { return table ? (g.KS > 1 ? g.partial_floats : 0) : m.partial_floats; }
 };
 
+// Default routing: one activation row goes to the table kernel unless its
+// plan needs a K split (a second reduce launch), where the matrix-core kernel,
+// which finishes its split in the same launch, is faster; 2..8 rows go to the
+// matrix-core kernel, with the table kernel as the fallback for shapes its
+// plan rejects.
 bool plan_packed(int M, int64_t N, int64_t K, bool pair, bool affine, PackedPlan* p, const char** why) {
-  p->table = use_table_kernel(M);
-  if (p->table) return q1::plan_gemv(M, N, K, pair, affine, &p->g, why);
-  return q1::plan_mma(M, N, K, pair, affine, &p->m, why);
+  const int env = packed_kernel_env();
+  if (env == 1) {
+    p->table = true;
+    return q1::plan_gemv(M, N, K, pair, affine, &p->g, why);
+  }
+  if (env == 2) {
+    p->table = false;
+    return q1::plan_mma(M, N, K, pair, affine, &p->m, why);
+  }
+  const char* why_t = nullptr;
+  const char* why_m = nullptr;
+  const bool ok_t = q1::plan_gemv(M, N, K, pair, affine, &p->g, &why_t);
+  const bool ok_m = q1::plan_mma(M, N, K, pair, affine, &p->m, &why_m);
+  if (M == 1)
+    p->table = ok_t && (p->g.KS == 1 || !ok_m);
+  else
+    p->table = !ok_m && ok_t;
+  if (!ok_t && !ok_m) {
+    *why = M == 1 ? why_t : why_m;
+    return false;
+  }
+  return true;
 }
 
 struct PackedWs {

@@ -54,6 +54,7 @@
 // order, so results never depend on timing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "q1_device.h"
@@ -146,18 +147,10 @@ __device__ __forceinline__ void prep_load(const MmaArgs& a, int span0, int nsp, 
 
 template <bool AFFINE>
 __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int tid, const PrepLoads& L) {
-  // rows no item writes: inactive A rows, their scales, lo/inactive sums
-  for (int idx = tid; idx < nsp * 512; idx += kThreads) {  // 16-byte A chunks
-    const int c = idx & 511, blk = c >> 6, pos = c & 63;
-    const int mrow = (pos & 15) ^ a_swz(pos >> 4, blk);
-    if ((mrow & 7) >= a.M) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(lds + (idx >> 9) * kSpanLds + a_blk_off(blk) + pos * 16) = z;
-    }
-  }
-  for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // scale dwords, one per lane
-    if (((idx & 15) & 7) >= a.M) reinterpret_cast<uint32_t*>(lds + (idx >> 6) * kSpanLds + kOffSc)[idx & 63] = 0x7f7f7f7fu;
-  }
+  // A rows of activation index >= M and their scales are never written: the
+  // MFMA keeps rows apart, so whatever they hold only reaches result rows that
+  // are never read.  The group sums enter as the accumulator input of every
+  // row and must be zero for the lo rows 8..15 (and are for rows >= M).
   for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // [g4][16] sums
     if ((idx & 15) >= a.M) reinterpret_cast<float*>(lds + (idx >> 6) * kSpanLds + kOffXs)[idx & 63] = 0.0f;
   }
@@ -323,6 +316,7 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   constexpr int NSC = SC128 ? 4 : 8;  // registers of metadata per row and item
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int last_flag;
+  __shared__ int wave_k0[kNW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -531,27 +525,39 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   }
 
   // ---- tile results: the slots of the waves that touched each tile, in
-  // wave order ----
+  // wave order.  Thread o takes (tile kk, activation row m, weight row r),
+  // rows fastest; the waves' first tiles come through LDS, so the loop does
+  // no integer division. ----
+  if (lane == 0) wave_k0[wave] = kfirst;
   lds_barrier();
-  for (int o = tid; o < nbp * 128; o += kThreads) {
-    const int kk = o >> 7, r = o & 127, ab = r >> 6, l = r & 63;
-    const int m = 4 * ((l >> 4) & 1) + 2 * ab + (l >> 5);
-    const int row = tile_of(kk) * 16 + (l & 15);
-    if (m >= a.M || row >= Nrows) continue;
-    const int t0 = kk * nds, t1 = t0 + nds;  // the tile's items
-    int wa = (t0 * kNW) / I;                 // first wave whose range can hold item t0
-    while (((wa + 1) * I) / kNW <= t0) ++wa;
-    float v[NMAT];
+  {
+    const int per_t = 16 * a.M;
+    const float inv_per_t = 1.0f / (float)per_t;
+    const float inv_I = I > 0 ? 1.0f / (float)I : 0.0f;
+    for (int o = tid; o < nbp * per_t; o += kThreads) {
+      const int kk = (int)(((float)o + 0.5f) * inv_per_t);  // o / per_t (exact: o < 2^22)
+      const int rem = o - kk * per_t;
+      const int m = rem >> 4, r = rem & 15;
+      const int row = tile_of(kk) * 16 + r;
+      if (row >= Nrows) continue;
+      const int t0 = kk * nds, t1 = t0 + nds;  // the tile's items
+      // wave holding item t0: the last w with w*I/8 <= t0 (estimate, then exact)
+      int wa = (int)((float)(8 * t0 + 7) * inv_I);
+      wa = wa > kNW - 1 ? kNW - 1 : wa;
+      while (wa > 0 && ((wa * I) >> 3) > t0) --wa;
+      while (wa < kNW - 1 && (((wa + 1) * I) >> 3) <= t0) ++wa;
+      const int l = r + 16 * ((m >> 2) & 1) + 32 * (m & 1), ab = (m >> 1) & 1;
+      float v[NMAT];
 #pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) v[mt] = 0.0f;
-    for (int w2 = wa; w2 < kNW && (w2 * I) / kNW < t1; ++w2) {
-      const int w_i0 = (w2 * I) / kNW;
-      if (((w2 + 1) * I) / kNW == w_i0) continue;  // wave without items
+      for (int mt = 0; mt < NMAT; ++mt) v[mt] = 0.0f;
+      for (int w2 = wa; w2 < kNW && ((w2 * I) >> 3) < t1; ++w2) {
+        if ((((w2 + 1) * I) >> 3) == ((w2 * I) >> 3)) continue;  // wave without items
+        const int sl = kk - wave_k0[w2];
 #pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt)
-        v[mt] += red[(((w2 * a.TW + (kk - w_i0 / nds)) * NMAT + mt) * 2 + ab) * 64 + l];
+        for (int mt = 0; mt < NMAT; ++mt) v[mt] += red[(((w2 * a.TW + sl) * NMAT + mt) * 2 + ab) * 64 + l];
+      }
+      emit(m, row, v);
     }
-    emit(m, row, v);
   }
   if (a.S == 1) return;
 
@@ -566,8 +572,10 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   lds_barrier();
   if (!last_flag) return;
   const int per_m = nbp * 16;
+  const float inv_per_m = 1.0f / (float)per_m;
   for (int o = tid; o < per_m * a.M; o += kThreads) {
-    const int m = o / per_m, rem = o - m * per_m;
+    const int m = (int)(((float)o + 0.5f) * inv_per_m);  // o / per_m (exact: o < 2^22)
+    const int rem = o - m * per_m;
     const int row = tile_of(rem >> 4) * 16 + (rem & 15);
     if (row >= Nrows) continue;
     float v[NMAT];
@@ -652,21 +660,13 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, c
   p->P = (int)P;
   p->nb = (int)((p->ntiles + P - 1) / P);  // tiles per workgroup (at most)
   p->wgs = (int64_t)p->S * P;
-  {  // most tiles one wave's item range touches, over every workgroup size
-     // (nbp <= nb tiles) and segment length (nds <= kds double spans)
-    int tw = 1;
-    for (int nbp = 1; nbp <= p->nb; ++nbp)
-      for (int nds = 1; nds <= kds; ++nds) {
-        const int64_t I = (int64_t)nbp * nds;
-        for (int w = 0; w < kNW; ++w) {
-          const int64_t i0 = w * I / kNW, i1 = (w + 1) * I / kNW;
-          if (i1 > i0) {
-            const int t = (int)((i1 - 1) / nds - i0 / nds + 1);
-            if (t > tw) tw = t;
-          }
-        }
-      }
-    p->TW = tw;
+  // Tiles one wave's item range [i0, i1) touches: floor((i1-1)/nds) -
+  // floor(i0/nds) + 1 < (i1-1-i0)/nds + 2 < nbp/8 + 2 for every workgroup
+  // size nbp <= nb and segment length nds, so at most ceil(nb/8) + 1.
+  p->TW = (int)std::min<int64_t>(p->nb, (p->nb + kNW - 1) / kNW + 1);
+  if ((int64_t)p->nb * 128 >= ((int64_t)1 << 22)) {
+    *why = "too many tiles per workgroup for the result slots";
+    return false;
   }
   p->red_bytes = (size_t)kNW * p->TW * nmat * 512;
   p->lds_bytes = (size_t)p->KSP * kSpanLds + p->red_bytes + (size_t)kNW * nmat * kScrDwords * 4;
