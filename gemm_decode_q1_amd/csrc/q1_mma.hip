@@ -114,6 +114,16 @@ __device__ __forceinline__ float dpp_half_mirror(float v) {  // lane i <- lane 7
 }
 
 
+// A register whose contents do not matter (the scaled conversions below
+// overwrite half of their destination and keep the other half; the first
+// conversion of each dword needs no old value).  The empty asm statement
+// hands over whatever the register holds instead of materialising a zero.
+__device__ __forceinline__ v2s undef_v2s() {
+  v2s r;
+  asm volatile("" : "=v"(r));
+  return r;
+}
+
 // Conversion of the activations of spans [span0, span0 + nsp) into the LDS
 // image.  Item = (row m, span, word, half word): 16 activations, one dword of
 // A bytes per bit class, for the hi and the lo piece.  The loads of all of a
@@ -198,12 +208,12 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
       const int e = sc - (j == 0 ? 1 : (j == 1 ? 0 : -1));  // 2^e = 2^sc / factor(j)
       const float dh = __uint_as_float((uint32_t)(e + 127) << 23);
       const float dl = __uint_as_float((uint32_t)(e + 123) << 23);
-      v2s h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, xv[j], xv[j + 4], dh, false);
+      v2s h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(undef_v2s(), xv[j], xv[j + 4], dh, false);
       h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, xv[j + 8], xv[j + 12], dh, true);
       const uint32_t hb = __builtin_bit_cast(uint32_t, h);
       const v2f d01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb, dh, false);
       const v2f d23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb, dh, true);
-      v2s l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, xv[j] - d01[0], xv[j + 4] - d01[1], dl, false);
+      v2s l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(undef_v2s(), xv[j] - d01[0], xv[j + 4] - d01[1], dl, false);
       l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, xv[j + 8] - d23[0], xv[j + 12] - d23[1], dl, true);
       hi[j] = hb;
       lo[j] = __builtin_bit_cast(uint32_t, l);
@@ -309,7 +319,10 @@ __device__ __forceinline__ float meta_at(const uint32_t* v, int g) {
 // 8 neighbouring lanes.  The MFMA B operand wants lane (n, q) = word q of every
 // group of row n: the words go through a per-wave LDS scratch (row stride 34
 // dwords: the 8-byte writes and 4-byte reads are bank-conflict free).
-template <bool AFFINE, bool MBF16, bool PAIR, bool SC128>
+// MR: accumulator rows per lane quarter that can hold a live activation row
+// (1 for M = 1, 2 for M = 2, else 4); the others are never read, so their
+// scale multiply-adds are skipped.
+template <bool AFFINE, bool MBF16, bool PAIR, bool SC128, int MR>
 __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   constexpr int NMAT = PAIR ? 2 : 1;
   constexpr int D = PAIR ? 2 : 4;
@@ -450,11 +463,11 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
         for (int g4 = 0; g4 < 4; ++g4) {
           const float sv = meta_at<MBF16, SC128>(sreg[u][mt], 4 * half + g4);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(sv, Dg[g4][i], acc[mt][i]);
+          for (int i = 0; i < MR; ++i) acc[mt][i] = fmaf(sv, Dg[g4][i], acc[mt][i]);
           if (AFFINE) {  // + b X
             const float bv = meta_at<MBF16, SC128>(breg[u][mt], 4 * half + g4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(bv, XS[g4][i], acc[mt][i]);
+            for (int i = 0; i < MR; ++i) acc[mt][i] = fmaf(bv, XS[g4][i], acc[mt][i]);
           }
         }
       }
@@ -608,20 +621,30 @@ int device_cus() {
   return cus;
 }
 
-template <bool AFFINE, bool MBF16, bool PAIR, bool SC128>
+template <bool AFFINE, bool MBF16, bool PAIR, bool SC128, int MR>
 hipError_t launch_k(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&q1_mma_kernel<AFFINE, MBF16, PAIR, SC128>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&q1_mma_kernel<AFFINE, MBF16, PAIR, SC128, MR>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 64);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((q1_mma_kernel<AFFINE, MBF16, PAIR, SC128>), dim3((unsigned)p.wgs), dim3(kThreads), p.lds_bytes,
-                     s, a);
+  hipLaunchKernelGGL((q1_mma_kernel<AFFINE, MBF16, PAIR, SC128, MR>), dim3((unsigned)p.wgs), dim3(kThreads),
+                     p.lds_bytes, s, a);
   return hipGetLastError();
+}
+
+template <bool AFFINE, bool MBF16, bool PAIR, bool SC128>
+hipError_t launch_r(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
+  if constexpr (PAIR) {
+    return launch_k<AFFINE, MBF16, PAIR, SC128, 4>(p, a, s);
+  } else {
+    if (a.M > 2) return launch_k<AFFINE, MBF16, PAIR, SC128, 4>(p, a, s);
+    return a.M == 1 ? launch_k<AFFINE, MBF16, PAIR, SC128, 1>(p, a, s) : launch_k<AFFINE, MBF16, PAIR, SC128, 2>(p, a, s);
+  }
 }
 
 template <bool AFFINE, bool MBF16, bool PAIR>
 hipError_t launch_t(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
-  return (a.G % 8 == 0) ? launch_k<AFFINE, MBF16, PAIR, true>(p, a, s) : launch_k<AFFINE, MBF16, PAIR, false>(p, a, s);
+  return (a.G % 8 == 0) ? launch_r<AFFINE, MBF16, PAIR, true>(p, a, s) : launch_r<AFFINE, MBF16, PAIR, false>(p, a, s);
 }
 
 }  // namespace
