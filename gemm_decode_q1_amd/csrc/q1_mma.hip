@@ -109,10 +109,39 @@ __device__ __forceinline__ float dpp_xor1(float v) {  // quad_perm [1,0,3,2]
 __device__ __forceinline__ float dpp_xor2(float v) {  // quad_perm [2,3,0,1]
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float dpp_half_mirror(float v) {  // lane i <- lane 7-i within 8
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xf, 0xf, false));
-}
 
+
+// Conversion of the activations of spans [span0, span0 + nsp) into the LDS
+// image.  Item = (row m, span, word): the 32 activations of one packed word's
+// weights, giving for the hi and the lo piece the two 16-byte A chunks of the
+// word (bit classes 0,1 and 2,3).  The loads of all of a thread's items (at
+// most kPrepRounds) are issued first (prep_load), so they can be in flight
+// together with the weight loads issued right after them.
+constexpr int kPrepRounds = 4;
+
+struct PrepLoads {
+  u32x4 q[kPrepRounds][4];
+};
+
+__device__ __forceinline__ void prep_load(const MmaArgs& a, int span0, int nsp, int tid, PrepLoads& L) {
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, a.x_bytes);
+  const int items = a.M * nsp * 16;
+  const float inv_nsp = 1.0f / (float)nsp;
+#pragma unroll
+  for (int r = 0; r < kPrepRounds; ++r) {
+    const int it = tid + r * kThreads;
+    const bool valid = it < items;
+    const int wi = it & 15, ms = it >> 4;
+    const int m = (int)(((float)ms + 0.5f) * inv_nsp);  // ms / nsp (exact: ms < 8 * kKspMax)
+    const int sp = ms - m * nsp;
+    const int k0 = (span0 + sp) * 512 + wi * 32;
+    const uint32_t off = (uint32_t)(((int64_t)m * a.x_ld + k0) * 2) | ((valid && k0 < a.K) ? 0u : kOOB);
+    if (r * kThreads < items) {  // uniform: skip rounds nobody needs
+#pragma unroll
+      for (int c = 0; c < 4; ++c) L.q[r][c] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16 * c, 0, 0);
+    }
+  }
+}
 
 // A register whose contents do not matter (the scaled conversions below
 // overwrite half of their destination and keep the other half; the first
@@ -124,37 +153,6 @@ __device__ __forceinline__ v2s undef_v2s() {
   return r;
 }
 
-// Conversion of the activations of spans [span0, span0 + nsp) into the LDS
-// image.  Item = (row m, span, word, half word): 16 activations, one dword of
-// A bytes per bit class, for the hi and the lo piece.  The loads of all of a
-// thread's items (at most kPrepRounds) are issued first (prep_load), so they
-// can be in flight together with the weight loads issued right after them.
-constexpr int kPrepRounds = 8;
-
-struct PrepLoads {
-  u32x4 q[kPrepRounds][2];
-};
-
-__device__ __forceinline__ void prep_load(const MmaArgs& a, int span0, int nsp, int tid, PrepLoads& L) {
-  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, a.x_bytes);
-  const int items = a.M * nsp * 32;
-  const float inv_nsp = 1.0f / (float)nsp;
-#pragma unroll
-  for (int r = 0; r < kPrepRounds; ++r) {
-    const int it = tid + r * kThreads;
-    const bool valid = it < items;
-    const int hh = it & 1, wi = (it >> 1) & 15, ms = it >> 5;
-    const int m = (int)(((float)ms + 0.5f) * inv_nsp);  // ms / nsp (exact: ms < 8 * kKspMax)
-    const int sp = ms - m * nsp;
-    const int k0 = (span0 + sp) * 512 + wi * 32 + hh * 16;
-    const uint32_t off = (uint32_t)(((int64_t)m * a.x_ld + k0) * 2) | ((valid && k0 < a.K) ? 0u : kOOB);
-    if (r * kThreads < items) {  // uniform: skip rounds nobody needs
-      L.q[r][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
-      L.q[r][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0);
-    }
-  }
-}
-
 template <bool AFFINE>
 __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int tid, const PrepLoads& L) {
   // A rows of activation index >= M and their scales are never written: the
@@ -164,12 +162,12 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
   for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // [g4][16] sums
     if ((idx & 15) >= a.M) reinterpret_cast<float*>(lds + (idx >> 6) * kSpanLds + kOffXs)[idx & 63] = 0.0f;
   }
-  const int items = a.M * nsp * 32;
-  // item = tid + 512 r: half word hh and word wi do not depend on the round;
-  // (row, span) index ms = tid/32 + 16 r is split by a rounded reciprocal
-  // (ms < 8 * kKspMax keeps it exact)
-  const int hh = tid & 1, wi = (tid >> 1) & 15;
+  const int items = a.M * nsp * 16;
+  // item = tid + 512 r: the word wi does not depend on the round; the (row,
+  // span) index ms = tid/16 + 32 r is split by a rounded reciprocal
+  const int wi = tid & 15;
   const int g4 = wi >> 2, b = wi & 3;
+  const int blk = 2 * g4 + (b >> 1);
   const float inv_nsp = 1.0f / (float)nsp;
   const v2bf ones = __builtin_bit_cast(v2bf, 0x3F803F80u);
 #pragma unroll
@@ -177,75 +175,71 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
     if (r * kThreads >= items) break;  // uniform; rounds with items keep whole waves (items % 64 == 0)
     const int it = tid + r * kThreads;
     const bool valid = it < items;
-    const int ms = it >> 5;
+    const int ms = it >> 4;
     const int m = (int)(((float)ms + 0.5f) * inv_nsp);
     const int sp = ms - m * nsp;
-    float xv[16];
+    // element t of the word (bit t) = dword t/2, half t%2
+    // (the group sum X starts here too: a bf16 pair dot (1, 1) per dword)
+    float xv[32];
+    float X = 0.0f;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const uint32_t wd = d < 4 ? L.q[r][0][d] : L.q[r][1][d - 4];
+    for (int d = 0; d < 16; ++d) {
+      const uint32_t wd = L.q[r][d >> 2][d & 3];
       xv[2 * d] = __uint_as_float(wd << 16);
       xv[2 * d + 1] = __uint_as_float(wd & 0xffff0000u);
+      X = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, wd), ones, X, false);
     }
-    // block scale from the word's largest |x| (the other half word is the
-    // neighbouring lane)
     float amax = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(xv[t]));
-    amax = fmaxf(amax, dpp_xor1(amax));
+    for (int t = 0; t < 32; ++t) amax = fmaxf(amax, fabsf(xv[t]));
     // |x| * 2^-sc < 2^7, at most 2^8 after the class factor: below the
     // largest fp8 value, 448.  The clamp keeps every divisor below a normal
     // fp32 power of two (bf16 data never reaches it at the top).
     int sc = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 7 : 0;
     sc = sc < -118 ? -118 : (sc > 125 ? 125 : sc);
-    // element t has bit position 16*hh + t in the word: class j = t % 4 goes
-    // to A bytes 4 apart (see the byte map below), times 1/code(j).  The
-    // scaled conversions divide by (and the decode multiplies by) a power of
-    // two: 2^sc / factor(j) for hi, 16 times less for lo.
-    uint32_t hi[4], lo[4];
+    // class j = t % 4, nibble i = t / 4, half word hh = i / 4: the 4 elements
+    // of (j, hh) become the 4 bytes of one dword, times 1/code(j).  The scaled
+    // conversions divide by (and the decode multiplies by) a power of two:
+    // 2^sc / factor(j) for hi, 16 times less for lo.
+    uint32_t hi[4][2], lo[4][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = sc - (j == 0 ? 1 : (j == 1 ? 0 : -1));  // 2^e = 2^sc / factor(j)
       const float dh = __uint_as_float((uint32_t)(e + 127) << 23);
       const float dl = __uint_as_float((uint32_t)(e + 123) << 23);
-      v2s h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(undef_v2s(), xv[j], xv[j + 4], dh, false);
-      h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, xv[j + 8], xv[j + 12], dh, true);
-      const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-      const v2f d01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb, dh, false);
-      const v2f d23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb, dh, true);
-      v2s l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(undef_v2s(), xv[j] - d01[0], xv[j + 4] - d01[1], dl, false);
-      l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, xv[j + 8] - d23[0], xv[j + 12] - d23[1], dl, true);
-      hi[j] = hb;
-      lo[j] = __builtin_bit_cast(uint32_t, l);
-    }
-    float X = 0.0f;
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
-      X = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, d < 4 ? L.q[r][0][d] : L.q[r][1][d - 4]), ones,
-                                          X, false);
-    // sum over the group's 8 items (4 words x 2 halves)
+      for (int hh = 0; hh < 2; ++hh) {
+        const float* v = xv + 16 * hh + j;  // v[0], v[4], v[8], v[12]
+        v2s h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(undef_v2s(), v[0], v[4], dh, false);
+        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, v[8], v[12], dh, true);
+        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+        const v2f d01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb, dh, false);
+        const v2f d23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb, dh, true);
+        v2s l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(undef_v2s(), v[0] - d01[0], v[4] - d01[1], dl, false);
+        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, v[8] - d23[0], v[12] - d23[1], dl, true);
+        hi[j][hh] = hb;
+        lo[j][hh] = __builtin_bit_cast(uint32_t, l);
+      }
+    }
+    // sum over the group's 4 words (neighbouring lanes)
     X += dpp_xor1(X);
     X += dpp_xor2(X);
-    X += dpp_half_mirror(X);
     if (valid) {
-      // A chunk (row, quarter qa, block (g4, h2)) holds in dword 2*(j & 1) +
-      // hh the class-j bytes of half word hh, where qa = 2*(b & 1) + (j >> 1)
-      // and h2 = b >> 1
+      // A chunk (row, quarter qa = 2*(b & 1) + c, block (g4, b >> 1)) holds in
+      // dword 2*(j & 1) + hh the class-j bytes of half word hh, j >> 1 == c
       unsigned char* base = lds + sp * kSpanLds;
-      const int blk = 2 * g4 + (b >> 1);
       unsigned char* bb = base + a_blk_off(blk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int qa = 2 * (b & 1) + (j >> 1), sw = a_swz(qa, blk);
-        const int dw = 2 * (j & 1) + hh;
-        *reinterpret_cast<uint32_t*>(bb + (qa * 16 + (m ^ sw)) * 16 + dw * 4) = hi[j];
-        *reinterpret_cast<uint32_t*>(bb + (qa * 16 + ((8 + m) ^ sw)) * 16 + dw * 4) = lo[j];
+      for (int c = 0; c < 2; ++c) {
+        const int qa = 2 * (b & 1) + c, sw = a_swz(qa, blk);
+        *reinterpret_cast<u32x4*>(bb + (qa * 16 + (m ^ sw)) * 16) =
+            u32x4{hi[2 * c][0], hi[2 * c][1], hi[2 * c + 1][0], hi[2 * c + 1][1]};
+        *reinterpret_cast<u32x4*>(bb + (qa * 16 + ((8 + m) ^ sw)) * 16) =
+            u32x4{lo[2 * c][0], lo[2 * c][1], lo[2 * c + 1][0], lo[2 * c + 1][1]};
       }
-      if (hh == 0) {
-        base[kOffSc + (m + 16 * b) * 4 + g4] = (unsigned char)(sc + 127);
-        base[kOffSc + (8 + m + 16 * b) * 4 + g4] = (unsigned char)(sc + 123);
-      }
-      if ((it & 7) == 0) reinterpret_cast<float*>(base + kOffXs)[g4 * 16 + m] = AFFINE ? X : -0.5f * X;
+      base[kOffSc + (m + 16 * b) * 4 + g4] = (unsigned char)(sc + 127);
+      base[kOffSc + (8 + m + 16 * b) * 4 + g4] = (unsigned char)(sc + 123);
+      if (b == 0) reinterpret_cast<float*>(base + kOffXs)[g4 * 16 + m] = AFFINE ? X : -0.5f * X;
     }
   }
 }
@@ -697,7 +691,7 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, c
     *why = "LDS budget exceeded";
     return false;
   }
-  if ((int64_t)M * p->KSP * 32 > (int64_t)kPrepRounds * kThreads) {
+  if ((int64_t)M * p->KSP * 16 > (int64_t)kPrepRounds * kThreads) {
     *why = "activation conversion exceeds its register rounds";
     return false;
   }
