@@ -72,25 +72,38 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kNW = 8;  // waves per workgroup
 constexpr int kThreads = kNW * 64;
-constexpr int kKspMax = 14;  // spans per K segment (LDS image 126 KB at most)
 
 // LDS image of one span (4 groups): A operand [g4][half][64 lanes][16 B],
 // block scales [64 lanes][4 groups] bytes, and the group sums of the
-// activations [g4][16 D rows] floats (-X/2 for symmetric tensors, X for affine)
-// (rows 8..15, the lo half, and rows of activation index >= M hold zeros;
-// inactive A rows hold zero bytes and unit scales).  Within each 1 KB block
-// (g4, half) the 16-byte chunk of lane 16*qa + row is stored at position
-// 16*qa + (row ^ a_swz(qa, block)), and the blocks of group g4 start 16*g4
-// bytes late: reads of 8 (or 16) consecutive lanes still cover distinct
-// banks, and the conversion's dword writes (one activation row, 4 words x 4
-// groups x 2 half words per instruction) spread over the banks too.
-constexpr int kSpanA = 4 * 2064;
-constexpr int kOffSc = kSpanA;
-constexpr int kOffXs = kOffSc + 256;
-constexpr int kSpanLds = kOffXs + 256;
-
+// activations [g4][16 D rows] floats (-X/2 for symmetric tensors, X for
+// affine; zero for the lo rows 8..15 and rows of activation index >= M).
+// With RB = 8 (any M) each 1 KB block (g4, half) stores the 16-byte chunk of
+// lane 16*qa + row at position 16*qa + (row ^ a_swz(qa, block)), and the
+// blocks of group g4 start 16*g4 bytes late: reads of 8 (or 16) consecutive
+// lanes still cover distinct banks, and the conversion's chunk writes (one
+// activation row per 16 lanes) spread over the banks too.  With RB = 1 or 2
+// (M = 1 or 2) only the live rows are stored: hi rows 0..RB-1 and lo rows
+// 8..8+RB-1, 2*RB chunks per quarter; the lanes of the other rows read the
+// chunk of row (row & (RB-1)) of their half (an LDS broadcast), which only
+// reaches MFMA result rows that are never read.  The smaller image lets one
+// workgroup hold a longer K segment.
 __device__ __forceinline__ int a_blk_off(int blk) { return blk * 1024 + (blk >> 1) * 16; }
 __device__ __forceinline__ int a_swz(int qa, int blk) { return qa | ((blk & 3) << 2); }
+
+template <int RB>
+struct ALay {
+  static constexpr int kA = RB == 8 ? 4 * 2064 : 1024 * RB;  // A operand bytes
+  static constexpr int kSc = kA;                              // block scales
+  static constexpr int kXs = kA + 256;                        // group sums
+  static constexpr int kSpan = kA + 512;                      // one span
+  // byte offset of the chunk of (block, quarter qa, tile row r); r is a live
+  // row for the writer, any row for a reader
+  static __device__ __forceinline__ int chunk(int blk, int qa, int r) {
+    if (RB == 8) return a_blk_off(blk) + (qa * 16 + (r ^ a_swz(qa, blk))) * 16;
+    return blk * (128 * RB) + (qa * 2 * RB + (r & (RB - 1)) + RB * (r >> 3)) * 16;
+  }
+};
+constexpr int span_bytes(int rb) { return rb == 8 ? 4 * 2064 + 512 : 1024 * rb + 512; }
 
 // per-wave LDS scratch of the word transpose: 16 rows x 34 dwords (32 used)
 constexpr int kScrStride = 34;
@@ -132,7 +145,7 @@ __device__ __forceinline__ void prep_load(const MmaArgs& a, int span0, int nsp, 
     const int it = tid + r * kThreads;
     const bool valid = it < items;
     const int wi = it & 15, ms = it >> 4;
-    const int m = (int)(((float)ms + 0.5f) * inv_nsp);  // ms / nsp (exact: ms < 8 * kKspMax)
+    const int m = (int)(((float)ms + 0.5f) * inv_nsp);  // ms / nsp (exact: ms < 2^20)
     const int sp = ms - m * nsp;
     const int k0 = (span0 + sp) * 512 + wi * 32;
     const uint32_t off = (uint32_t)(((int64_t)m * a.x_ld + k0) * 2) | ((valid && k0 < a.K) ? 0u : kOOB);
@@ -153,14 +166,15 @@ __device__ __forceinline__ v2s undef_v2s() {
   return r;
 }
 
-template <bool AFFINE>
+template <bool AFFINE, int RB>
 __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int tid, const PrepLoads& L) {
+  using Lay = ALay<RB>;
   // A rows of activation index >= M and their scales are never written: the
   // MFMA keeps rows apart, so whatever they hold only reaches result rows that
   // are never read.  The group sums enter as the accumulator input of every
   // row and must be zero for the lo rows 8..15 (and are for rows >= M).
   for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // [g4][16] sums
-    if ((idx & 15) >= a.M) reinterpret_cast<float*>(lds + (idx >> 6) * kSpanLds + kOffXs)[idx & 63] = 0.0f;
+    if ((idx & 15) >= a.M) reinterpret_cast<float*>(lds + (idx >> 6) * Lay::kSpan + Lay::kXs)[idx & 63] = 0.0f;
   }
   const int items = a.M * nsp * 16;
   // item = tid + 512 r: the word wi does not depend on the round; the (row,
@@ -227,19 +241,18 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
     if (valid) {
       // A chunk (row, quarter qa = 2*(b & 1) + c, block (g4, b >> 1)) holds in
       // dword 2*(j & 1) + hh the class-j bytes of half word hh, j >> 1 == c
-      unsigned char* base = lds + sp * kSpanLds;
-      unsigned char* bb = base + a_blk_off(blk);
+      unsigned char* base = lds + sp * Lay::kSpan;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const int qa = 2 * (b & 1) + c, sw = a_swz(qa, blk);
-        *reinterpret_cast<u32x4*>(bb + (qa * 16 + (m ^ sw)) * 16) =
+        const int qa = 2 * (b & 1) + c;
+        *reinterpret_cast<u32x4*>(base + Lay::chunk(blk, qa, m)) =
             u32x4{hi[2 * c][0], hi[2 * c][1], hi[2 * c + 1][0], hi[2 * c + 1][1]};
-        *reinterpret_cast<u32x4*>(bb + (qa * 16 + ((8 + m) ^ sw)) * 16) =
+        *reinterpret_cast<u32x4*>(base + Lay::chunk(blk, qa, 8 + m)) =
             u32x4{lo[2 * c][0], lo[2 * c][1], lo[2 * c + 1][0], lo[2 * c + 1][1]};
       }
-      base[kOffSc + (m + 16 * b) * 4 + g4] = (unsigned char)(sc + 127);
-      base[kOffSc + (8 + m + 16 * b) * 4 + g4] = (unsigned char)(sc + 123);
-      if (b == 0) reinterpret_cast<float*>(base + kOffXs)[g4 * 16 + m] = AFFINE ? X : -0.5f * X;
+      base[Lay::kSc + (m + 16 * b) * 4 + g4] = (unsigned char)(sc + 127);
+      base[Lay::kSc + (8 + m + 16 * b) * 4 + g4] = (unsigned char)(sc + 123);
+      if (b == 0) reinterpret_cast<float*>(base + Lay::kXs)[g4 * 16 + m] = AFFINE ? X : -0.5f * X;
     }
   }
 }
@@ -318,6 +331,8 @@ __device__ __forceinline__ float meta_at(const uint32_t* v, int g) {
 // scale multiply-adds are skipped.
 template <bool AFFINE, bool MBF16, bool PAIR, bool SC128, int MR>
 __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
+  constexpr int RB = MR == 4 ? 8 : MR;  // A rows kept in LDS per half
+  using Lay = ALay<RB>;
   constexpr int NMAT = PAIR ? 2 : 1;
   constexpr int D = PAIR ? 2 : 4;
   constexpr int NSC = SC128 ? 4 : 8;  // registers of metadata per row and item
@@ -338,8 +353,8 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   const int I = nbp * nds;                                          // items of this workgroup
   const int i0 = (wave * I) / kNW, i1 = ((wave + 1) * I) / kNW;
   const int nitems = i1 - i0;
-  float* red = reinterpret_cast<float*>(lds + (size_t)a.KSP * kSpanLds);  // [w][slot][mt][ab][64]
-  uint32_t* scr = reinterpret_cast<uint32_t*>(lds + (size_t)a.KSP * kSpanLds + (size_t)a.red_bytes) +
+  float* red = reinterpret_cast<float*>(lds + (size_t)a.KSP * Lay::kSpan);  // [w][slot][mt][ab][64]
+  uint32_t* scr = reinterpret_cast<uint32_t*>(lds + (size_t)a.KSP * Lay::kSpan + (size_t)a.red_bytes) +
                   wave * (NMAT * kScrDwords);
 
   const __amdgpu_buffer_rsrc_t rp[2] = {rsrc(a.p0, a.packed_bytes), rsrc(PAIR ? a.p1 : a.p0, a.packed_bytes)};
@@ -351,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   const int q = lane >> 4;    // lane quarter
   const int lr = lane >> 3;   // row within a load instruction
   const int lc = lane & 7;    // 16-byte chunk (group) within a row's 128 bytes
-  const int lane_sw = lane ^ q;  // A chunk position of this lane, before the block's part of the swizzle
+  const int a_lane0 = Lay::chunk(0, q, nl);  // (RB < 8) this lane's A chunk within a block
   const uint32_t row_bytes = (uint32_t)a.K >> 3;
   // row indices fit in 31 bits (the plan keeps N*K/8 below 2^31)
   const int Nrows = (int)a.N;
@@ -403,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
       }
     }
   }
-  prep_compute<AFFINE>(a, 2 * nds, lds, tid, pl);
+  prep_compute<AFFINE, RB>(a, 2 * nds, lds, tid, pl);
   lds_barrier();
 
   auto compute = [&](int u, int d) {
@@ -423,16 +438,23 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const unsigned char* base = lds + (2 * d + half) * kSpanLds;
-      const uint32_t scale_a = reinterpret_cast<const uint32_t*>(base + kOffSc)[lane];
+      const unsigned char* base = lds + (2 * d + half) * Lay::kSpan;
+      const uint32_t scale_a = reinterpret_cast<const uint32_t*>(base + Lay::kSc)[lane];
       v8i A[4];
       v4f XS[4];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const u32x4 h0 = reinterpret_cast<const u32x4*>(base + a_blk_off(2 * g4))[lane_sw ^ ((g4 & 1) << 3)];
-        const u32x4 h1 = reinterpret_cast<const u32x4*>(base + a_blk_off(2 * g4 + 1))[lane_sw ^ (4 | ((g4 & 1) << 3))];
+        u32x4 h0, h1;
+        if (RB == 8) {
+          const int lane_sw = lane ^ q;  // position before the block's part of the swizzle
+          h0 = reinterpret_cast<const u32x4*>(base + a_blk_off(2 * g4))[lane_sw ^ ((g4 & 1) << 3)];
+          h1 = reinterpret_cast<const u32x4*>(base + a_blk_off(2 * g4 + 1))[lane_sw ^ (4 | ((g4 & 1) << 3))];
+        } else {
+          h0 = *reinterpret_cast<const u32x4*>(base + 2 * g4 * (128 * RB) + a_lane0);
+          h1 = *reinterpret_cast<const u32x4*>(base + (2 * g4 + 1) * (128 * RB) + a_lane0);
+        }
         A[g4] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-        XS[g4] = reinterpret_cast<const v4f*>(base + kOffXs)[g4 * 4 + q];
+        XS[g4] = reinterpret_cast<const v4f*>(base + Lay::kXs)[g4 * 4 + q];
       }
       const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -666,37 +688,53 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, c
   p->nspan = (p->G + 3) / 4;
   p->ntiles = (N + 15) / 16;
   const int ndsp = (p->nspan + 1) / 2;  // double spans
-  const int kdmax = kKspMax / 2;
-  p->S = (ndsp + kdmax - 1) / kdmax;
-  const int kds = (ndsp + p->S - 1) / p->S;
-  p->S = (ndsp + kds - 1) / kds;
-  p->KSP = 2 * kds;
-  int64_t P = p->ntiles;
-  const int64_t cap = cus / p->S > 0 ? cus / p->S : 1;
-  if (P > cap) P = cap;
-  p->P = (int)P;
-  p->nb = (int)((p->ntiles + P - 1) / P);  // tiles per workgroup (at most)
-  p->wgs = (int64_t)p->S * P;
-  // Tiles one wave's item range [i0, i1) touches: floor((i1-1)/nds) -
-  // floor(i0/nds) + 1 < (i1-1-i0)/nds + 2 < nbp/8 + 2 for every workgroup
-  // size nbp <= nb and segment length nds, so at most ceil(nb/8) + 1.
-  p->TW = (int)std::min<int64_t>(p->nb, (p->nb + kNW - 1) / kNW + 1);
+  const int rb = (pair || M > 2) ? 8 : M;
+  const size_t span = (size_t)span_bytes(rb);
+  const size_t scratch = (size_t)kNW * nmat * kScrDwords * 4;
+  const size_t budget = 160 * 1024 - 64;
+  // Number of K segments S: among the splits whose LDS image, result slots
+  // and scratch fit, the one with the fewest items in the busiest workgroup
+  // (tiles are whole per workgroup, so S also balances the work), where a
+  // split (the partial sums' round trips at the end, S partials per result)
+  // counts as 6 + S/2 items (measured on the shapes with 17408-weight rows).
+  MmaPlan best;
+  int64_t best_cost = -1;
+  for (int S = 1; S <= ndsp; ++S) {
+    MmaPlan c = *p;
+    const int kds = (ndsp + S - 1) / S;
+    c.S = (ndsp + kds - 1) / kds;
+    if (c.S != S) continue;  // same split as a smaller S
+    c.KSP = 2 * kds;
+    int64_t P = c.ntiles;
+    const int64_t cap = cus / c.S > 0 ? cus / c.S : 1;
+    if (P > cap) P = cap;
+    c.P = (int)P;
+    c.nb = (int)((c.ntiles + P - 1) / P);  // tiles per workgroup (at most)
+    c.wgs = (int64_t)c.S * P;
+    // Tiles one wave's item range [i0, i1) touches: floor((i1-1)/nds) -
+    // floor(i0/nds) + 1 < (i1-1-i0)/nds + 2 < nbp/8 + 2 for every workgroup
+    // size nbp <= nb and segment length nds, so at most ceil(nb/8) + 1.
+    c.TW = (int)std::min<int64_t>(c.nb, (c.nb + kNW - 1) / kNW + 1);
+    c.red_bytes = (size_t)kNW * c.TW * nmat * 512;
+    c.lds_bytes = (size_t)c.KSP * span + c.red_bytes + scratch;
+    if (c.lds_bytes > budget || (int64_t)M * c.KSP * 16 > (int64_t)kPrepRounds * kThreads) continue;
+    const int64_t cost = (int64_t)c.nb * kds + (c.S > 1 ? 6 + c.S / 2 : 0);
+    if (best_cost < 0 || cost < best_cost) {
+      best = c;
+      best_cost = cost;
+    }
+  }
+  if (best_cost < 0) {
+    *why = "LDS budget exceeded";
+    return false;
+  }
+  *p = best;
   if ((int64_t)p->nb * 128 >= ((int64_t)1 << 22)) {
     *why = "too many tiles per workgroup for the result slots";
     return false;
   }
-  p->red_bytes = (size_t)kNW * p->TW * nmat * 512;
-  p->lds_bytes = (size_t)p->KSP * kSpanLds + p->red_bytes + (size_t)kNW * nmat * kScrDwords * 4;
-  if (p->lds_bytes > 160 * 1024 - 64) {
-    *why = "LDS budget exceeded";
-    return false;
-  }
-  if ((int64_t)M * p->KSP * 16 > (int64_t)kPrepRounds * kThreads) {
-    *why = "activation conversion exceeds its register rounds";
-    return false;
-  }
   p->partial_floats = p->S > 1 ? (size_t)p->S * M * N * nmat : 0;
-  p->counters = p->S > 1 ? (size_t)P : 0;  // one per workgroup column p (P <= CUs)
+  p->counters = p->S > 1 ? (size_t)p->P : 0;  // one per workgroup column p (P <= CUs)
   return true;
 }
 

@@ -93,11 +93,11 @@ def test_empty_batch_is_a_no_op():
 def test_workspace_validation():
     w = weight(K=17408, N=5120)
     L = B.load_library()
-    need = L.q1_qmm_workspace_bytes(1, ctypes.byref(w))
-    assert need > 0  # 17 chunks of K need a split: partial sums + counters
-    st, err = qmm(w, M=1)
+    need = L.q1_qmm_workspace_bytes(4, ctypes.byref(w))
+    assert need > 0  # 4 rows, 17408 weights per row: a K split (partial sums + counters)
+    st, err = qmm(w, M=4)
     assert st == 3 and "workspace too small" in err
-    st, err = qmm(w, M=1, ws=FAKE, wsb=need - 1)
+    st, err = qmm(w, M=4, ws=FAKE, wsb=need - 1)
     assert st == 3
     wide = L.q1_qmm_workspace_bytes(9, ctypes.byref(w))
     assert wide >= 5120 * 17408 * 2  # dense bf16 copy for the fallback
