@@ -129,6 +129,16 @@ int packed_kernel_env() {
   return v;
 }
 
+// More than 8 rows: the wide matrix-core kernel straight from the packed
+// weights; Q1_WIDE_KERNEL=dequant selects the dequantise-to-bf16 + GEMM path.
+bool use_wide_kernel() {
+  static const bool v = [] {
+    const char* e = getenv("Q1_WIDE_KERNEL");
+    return !(e && strcmp(e, "dequant") == 0);
+  }();
+  return v;
+}
+
 struct PackedPlan {
   bool table;
   q1::GemvPlan g;
@@ -182,7 +192,9 @@ struct FfnWs {
   PackedPlan pgu, pg, pu, pd;
   size_t h_off, gu_off, d_off;     // packed: counters+partials blocks
   size_t g_off, u_off;             // unfused / wide: fp32 g and u
-  size_t deq_off;                  // wide: dequantised matrix
+  size_t deq_off;                  // wide: operand image (matrix-core path) or dequantised matrix
+  bool wide_mma;                   // wide: matrix-core path
+  q1::WidePlan wg, wu, wd;
   size_t bytes;
 };
 
@@ -193,6 +205,7 @@ bool same_format(const q1_weight* a, const q1_weight* b) {
 q1_status ffn_layout(int64_t M, const q1_weight* gate, const q1_weight* up, const q1_weight* down, FfnWs* L) {
   const int64_t I = gate->N, H = gate->K, Ho = down->N;
   L->packed = M <= g_max_rows;
+  L->wide_mma = false;
   L->fused = L->packed && same_format(gate, up);
   L->h_off = kReserved;
   size_t off = align_up(kReserved + (size_t)M * I * 2, 256);
@@ -224,9 +237,19 @@ q1_status ffn_layout(int64_t M, const q1_weight* gate, const q1_weight* up, cons
     L->u_off = off;
     off = align_up(off + (size_t)M * I * 4, 256);
     L->deq_off = off;
-    size_t big = (size_t)I * H;
-    if ((size_t)Ho * I > big) big = (size_t)Ho * I;
-    off = align_up(off + big * 2, 256);
+    L->wide_mma = use_wide_kernel() && q1::plan_wide(M, I, H, !gate->symmetric, &L->wg, &why) &&
+                  q1::plan_wide(M, up->N, up->K, !up->symmetric, &L->wu, &why) &&
+                  q1::plan_wide(M, Ho, I, !down->symmetric, &L->wd, &why);
+    if (L->wide_mma) {
+      size_t big = L->wg.ws_bytes;
+      if (L->wu.ws_bytes > big) big = L->wu.ws_bytes;
+      if (L->wd.ws_bytes > big) big = L->wd.ws_bytes;
+      off = align_up(off + big, 256);
+    } else {
+      size_t big = (size_t)I * H;
+      if ((size_t)Ho * I > big) big = (size_t)Ho * I;
+      off = align_up(off + big * 2, 256);
+    }
   }
   L->bytes = off;
   return Q1_OK;
@@ -291,6 +314,9 @@ size_t q1_qmm_workspace_bytes(int64_t M, const q1_weight* w) {
     const size_t part = packed_ws(p, kReserved).bytes;
     return part ? kReserved + part : 0;
   }
+  q1::WidePlan wp;
+  const char* why = "";
+  if (use_wide_kernel() && q1::plan_wide(M, w->N, w->K, !w->symmetric, &wp, &why)) return kReserved + wp.ws_bytes;
   return kReserved + align_up((size_t)w->N * w->K * 2, 256);
 }
 
@@ -320,6 +346,11 @@ q1_status q1_qmm(const void* x, int32_t x_dtype, int64_t M, const q1_weight* w, 
     if (!plan_packed((int)M, w->N, w->K, false, !w->symmetric, &p, &why)) return fail(Q1_ERR_UNSUPPORTED, "%s", why);
     return run_packed(p, static_cast<const uint16_t*>(x), w->K, a, nullptr, y, y_dtype, w->N, ws, kReserved, s);
   }
+  q1::WidePlan wp;
+  const char* why = "";
+  if (use_wide_kernel() && q1::plan_wide(M, w->N, w->K, !w->symmetric, &wp, &why))
+    return hip_status(q1::launch_wide(wp, static_cast<const uint16_t*>(x), w->K, a, y, y_dtype, w->N, ws + kReserved, s),
+                      "wide launch");
   uint16_t* deq = reinterpret_cast<uint16_t*>(ws + kReserved);
   hipError_t e = q1::launch_dequant(a, nullptr, 0, w->N, deq, q1::BF16, s);
   if (e != hipSuccess) return hip_status(e, "dequant launch");
@@ -414,6 +445,14 @@ q1_status q1_ffn(const void* x, int64_t M, const q1_weight* gate, const q1_weigh
   }
   float* gf = reinterpret_cast<float*>(ws + L.g_off);
   float* uf = reinterpret_cast<float*>(ws + L.u_off);
+  if (L.wide_mma) {  // the operand image region is reused by the three products in turn
+    unsigned char* img = ws + L.deq_off;
+    hipError_t e = q1::launch_wide(L.wg, xb, H, g, gf, q1::F32, I, img, s);
+    if (e == hipSuccess) e = q1::launch_wide(L.wu, xb, H, u, uf, q1::F32, I, img, s);
+    if (e == hipSuccess) e = q1::launch_silu_mul(gf, uf, h, M * I, s);
+    if (e == hipSuccess) e = q1::launch_wide(L.wd, h, I, d, y, q1::BF16, Ho, img, s);
+    return hip_status(e, "wide FFN launch");
+  }
   uint16_t* deq = reinterpret_cast<uint16_t*>(ws + L.deq_off);
   hipError_t e = q1::launch_dequant(g, nullptr, 0, I, deq, q1::BF16, s);
   if (e == hipSuccess) e = q1::launch_gemm_bf16(xb, deq, M, I, H, gf, q1::F32, s);

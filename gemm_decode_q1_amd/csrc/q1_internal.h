@@ -148,6 +148,23 @@ hipError_t launch_dequant(const QMat& w, const void* ids, int ids_int64, int64_t
                           hipStream_t stream);
 
 // y[M, N] (bf16 or fp32) = x[M, K] (bf16) * B[N, K]^T (bf16), fp32 accumulate.
+// Plan of one wide (M > 8) matrix-core launch pair (activation image, then
+// the product straight from the packed weights; see q1_wide.hip).
+struct WidePlan {
+  int64_t M, N;
+  int K, G, nspan;
+  int MB;      // row blocks of 8 activation rows
+  int mtiles;  // workgroups along M (8 row blocks each)
+  int tnb;     // 16-row column blocks per workgroup
+  int ntn;     // workgroups along N
+  int64_t wgs;
+  size_t sc_off, xs_off, ws_bytes;  // workspace: A image, scale image, group sums
+};
+
+bool plan_wide(int64_t M, int64_t N, int64_t K, bool affine, WidePlan* plan, const char** why);
+hipError_t launch_wide(const WidePlan& plan, const uint16_t* x, int64_t x_ld, const QMat& w, void* out,
+                       int32_t out_dtype, int64_t out_ld, unsigned char* ws, hipStream_t stream);
+
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* B, int64_t M, int64_t N, int64_t K, void* y,
                             int32_t y_dtype, hipStream_t stream);
 

@@ -58,6 +58,7 @@
 #include <cstdint>
 
 #include "q1_device.h"
+#include "q1_fp8.h"
 #include "q1_internal.h"
 
 namespace q1 {
@@ -66,9 +67,6 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef short v2s __attribute__((ext_vector_type(2)));
-typedef float v2f __attribute__((ext_vector_type(2)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kNW = 8;  // waves per workgroup
 constexpr int kThreads = kNW * 64;
@@ -156,16 +154,6 @@ __device__ __forceinline__ void prep_load(const MmaArgs& a, int span0, int nsp, 
   }
 }
 
-// A register whose contents do not matter (the scaled conversions below
-// overwrite half of their destination and keep the other half; the first
-// conversion of each dword needs no old value).  The empty asm statement
-// hands over whatever the register holds instead of materialising a zero.
-__device__ __forceinline__ v2s undef_v2s() {
-  v2s r;
-  asm volatile("" : "=v"(r));
-  return r;
-}
-
 template <bool AFFINE, int RB>
 __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int tid, const PrepLoads& L) {
   using Lay = ALay<RB>;
@@ -183,7 +171,6 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
   const int g4 = wi >> 2, b = wi & 3;
   const int blk = 2 * g4 + (b >> 1);
   const float inv_nsp = 1.0f / (float)nsp;
-  const v2bf ones = __builtin_bit_cast(v2bf, 0x3F803F80u);
 #pragma unroll
   for (int r = 0; r < kPrepRounds; ++r) {
     if (r * kThreads >= items) break;  // uniform; rounds with items keep whole waves (items % 64 == 0)
@@ -192,49 +179,13 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
     const int ms = it >> 4;
     const int m = (int)(((float)ms + 0.5f) * inv_nsp);
     const int sp = ms - m * nsp;
-    // element t of the word (bit t) = dword t/2, half t%2
-    // (the group sum X starts here too: a bf16 pair dot (1, 1) per dword)
-    float xv[32];
-    float X = 0.0f;
+    uint32_t wd[16];
 #pragma unroll
-    for (int d = 0; d < 16; ++d) {
-      const uint32_t wd = L.q[r][d >> 2][d & 3];
-      xv[2 * d] = __uint_as_float(wd << 16);
-      xv[2 * d + 1] = __uint_as_float(wd & 0xffff0000u);
-      X = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, wd), ones, X, false);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 32; ++t) amax = fmaxf(amax, fabsf(xv[t]));
-    // |x| * 2^-sc < 2^7, at most 2^8 after the class factor: below the
-    // largest fp8 value, 448.  The clamp keeps every divisor below a normal
-    // fp32 power of two (bf16 data never reaches it at the top).
-    int sc = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 7 : 0;
-    sc = sc < -118 ? -118 : (sc > 125 ? 125 : sc);
-    // class j = t % 4, nibble i = t / 4, half word hh = i / 4: the 4 elements
-    // of (j, hh) become the 4 bytes of one dword, times 1/code(j).  The scaled
-    // conversions divide by (and the decode multiplies by) a power of two:
-    // 2^sc / factor(j) for hi, 16 times less for lo.
+    for (int d = 0; d < 16; ++d) wd[d] = L.q[r][d >> 2][d & 3];
     uint32_t hi[4][2], lo[4][2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = sc - (j == 0 ? 1 : (j == 1 ? 0 : -1));  // 2^e = 2^sc / factor(j)
-      const float dh = __uint_as_float((uint32_t)(e + 127) << 23);
-      const float dl = __uint_as_float((uint32_t)(e + 123) << 23);
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const float* v = xv + 16 * hh + j;  // v[0], v[4], v[8], v[12]
-        v2s h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(undef_v2s(), v[0], v[4], dh, false);
-        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, v[8], v[12], dh, true);
-        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-        const v2f d01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb, dh, false);
-        const v2f d23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb, dh, true);
-        v2s l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(undef_v2s(), v[0] - d01[0], v[4] - d01[1], dl, false);
-        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, v[8] - d23[0], v[12] - d23[1], dl, true);
-        hi[j][hh] = hb;
-        lo[j][hh] = __builtin_bit_cast(uint32_t, l);
-      }
-    }
+    int sc;
+    float X;
+    q1_convert_word(wd, hi, lo, sc, X);
     // sum over the group's 4 words (neighbouring lanes)
     X += dpp_xor1(X);
     X += dpp_xor2(X);

@@ -100,7 +100,8 @@ def test_workspace_validation():
     st, err = qmm(w, M=4, ws=FAKE, wsb=need - 1)
     assert st == 3
     wide = L.q1_qmm_workspace_bytes(9, ctypes.byref(w))
-    assert wide >= 5120 * 17408 * 2  # dense bf16 copy for the fallback
+    # 9 rows: two blocks of 8 rows, each 2 KB of fp8 operand per 128-weight group
+    assert wide >= 2 * (17408 // 128) * 2048
 
 
 def test_dequant_and_gather_validation():
@@ -137,7 +138,8 @@ def test_max_packed_rows_setter():
         assert L.q1_set_max_packed_rows(0) == -1
         assert L.q1_set_max_packed_rows(9) == -1
         w = weight(K=1024, N=64)
-        # M = 5 now goes to the dense fallback, whose workspace is the bf16 copy
-        assert L.q1_qmm_workspace_bytes(5, ctypes.byref(w)) >= 64 * 1024 * 2
+        # M = 5 now goes to the wide path, whose workspace holds the fp8
+        # operand image of one 8-row block (2 KB per 128-weight group)
+        assert L.q1_qmm_workspace_bytes(5, ctypes.byref(w)) >= (1024 // 128) * 2048
     finally:
         L.q1_set_max_packed_rows(prev)
