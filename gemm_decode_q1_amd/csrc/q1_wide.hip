@@ -149,6 +149,7 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
   __shared__ __align__(16) unsigned char wsm[2][ROWS * kRowB];
   __shared__ __align__(16) uint32_t ssm[2][ROWS * 2];  // 4 fp16/bf16 scales per row
   __shared__ __align__(16) uint32_t bsm[AFFINE ? 2 : 1][AFFINE ? ROWS * 2 : 2];
+  __shared__ __align__(16) float xsm[2][kWaves * 4 * 16];  // group sums of a span: [row block][group][row]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -171,6 +172,7 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
   // ---- staging of span sp's weights: thread -> (row, group chunk) ----
   u32x4 wreg[LOADS];
   uint32_t sreg[2], breg[2];
+  float xreg;
   auto stage_load = [&](int sp) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -181,6 +183,11 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
       const bool ok = row < ROWS && n < a.N && g < a.G;
       const uint32_t off = ((uint32_t)n * row_bytes + (uint32_t)g * 16u) | (ok ? 0u : kOOB);
       wreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 2);
+    }
+    {  // group sums: thread -> (row block, group, row)
+      const int rbl = tid >> 6, g = 4 * sp + ((tid >> 4) & 3);
+      const int rbg = tm * kWaves + rbl;
+      xreg = (rbg < a.MB && g < a.G) ? a.xs_img[((int64_t)rbg * a.G + g) * 16 + (tid & 15)] : 0.0f;
     }
     // scales (and biases) of groups 4sp..4sp+3, one row per thread
     const int row = tid;
@@ -211,6 +218,7 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
         for (int k = 0; k < 4; ++k) dst[4 * k] = wreg[i][k];  // word k of group c -> [k][c]
       }
     }
+    xsm[buf][tid] = xreg;
     if (tid < ROWS) {
       ssm[buf][2 * tid] = sreg[0];
       ssm[buf][2 * tid + 1] = sreg[1];
@@ -223,9 +231,8 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
 
   // ---- this wave's A operands for span sp (4 groups) ----
   v8i A[4];
-  v4f XS[4];
   uint32_t scale_a = 0;
-  auto a_load = [&](int sp, v8i (&Ao)[4], v4f (&Xo)[4], uint32_t& so) {
+  auto a_load = [&](int sp, v8i (&Ao)[4], uint32_t& so) {
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
       const int g = 4 * sp + gi;
@@ -233,10 +240,8 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
         const u32x4* t = reinterpret_cast<const u32x4*>(a.img + (((int64_t)rb * a.G + g) * 64 + lane) * 32);
         const u32x4 h0 = t[0], h1 = t[1];
         Ao[gi] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-        Xo[gi] = reinterpret_cast<const v4f*>(a.xs_img + ((int64_t)rb * a.G + g) * 16)[q];
       } else {
         Ao[gi] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        Xo[gi] = v4f{0.f, 0.f, 0.f, 0.f};
       }
     }
     so = a.sc_img[((int64_t)rb * a.nspan + sp) * 64 + lane];
@@ -247,18 +252,17 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
   for (int j = 0; j < TNB; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   stage_load(0);
-  if (live) a_load(0, A, XS, scale_a);
+  if (live) a_load(0, A, scale_a);
   stage_store(0);
   lds_barrier();
 
   for (int sp = 0; sp < a.nspan; ++sp) {
     const int buf = sp & 1;
     v8i An[4];
-    v4f Xn[4];
     uint32_t sn = 0;
     if (sp + 1 < a.nspan) {
       stage_load(sp + 1);
-      if (live) a_load(sp + 1, An, Xn, sn);
+      if (live) a_load(sp + 1, An, sn);
     }
     if (live) {
       // groups past G (last span) have zero A operands, zero weights and zero
@@ -268,6 +272,24 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
       auto rd_s = [&](int j) { return *reinterpret_cast<const u32x2*>(&ssm[buf][2 * (j * 16 + nl)]); };
       auto rd_b = [&](int j) {
         return AFFINE ? *reinterpret_cast<const u32x2*>(&bsm[buf][2 * (j * 16 + nl)]) : u32x2{0u, 0u};
+      };
+      v4f XS[4];  // this wave's group sums of the span, rows 4q..4q+3
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) XS[gi] = reinterpret_cast<const v4f*>(&xsm[buf][(wave * 4 + gi) * 16])[q];
+      v4f Dp[4];
+      u32x2 s4p = {0u, 0u}, b4p = {0u, 0u};
+      auto fma_block = [&](int j, const v4f (&Dv)[4], u32x2 sv4, u32x2 bv4) {
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          const float sv = meta_val<MBF16>(sv4[gi >> 1] >> (16 * (gi & 1)));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(sv, Dv[gi][i], acc[j][i]);
+          if (AFFINE) {
+            const float bv = meta_val<MBF16>(bv4[gi >> 1] >> (16 * (gi & 1)));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(bv, XS[gi][i], acc[j][i]);
+          }
+        }
       };
       u32x4 w4n = rd_w(0);  // word q of groups 0..3
       u32x2 s4n = rd_s(0), b4n = rd_b(0);
@@ -296,18 +318,15 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
           else
             D[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[3], B, C, 0, 4, 3, (int)scale_a, 0, 0x7f7f7f7f);
         }
+        // the scale multiply-adds of block j-1 go after block j's products,
+        // so they never wait for a product just issued
+        if (j > 0) fma_block(j - 1, Dp, s4p, b4p);
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const float sv = meta_val<MBF16>(s4[gi >> 1] >> (16 * (gi & 1)));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(sv, D[gi][i], acc[j][i]);
-          if (AFFINE) {
-            const float bv = meta_val<MBF16>(b4[gi >> 1] >> (16 * (gi & 1)));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(bv, XS[gi][i], acc[j][i]);
-          }
-        }
+        for (int gi = 0; gi < 4; ++gi) Dp[gi] = D[gi];
+        s4p = s4;
+        b4p = b4;
       }
+      fma_block(TNB - 1, Dp, s4p, b4p);
     }
     if (sp + 1 < a.nspan) stage_store(buf ^ 1);  // that buffer was last read before the previous barrier
     lds_barrier();
@@ -315,7 +334,6 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         A[gi] = An[gi];
-        XS[gi] = Xn[gi];
       }
       scale_a = sn;
     }
