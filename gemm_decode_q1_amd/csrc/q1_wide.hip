@@ -6,21 +6,22 @@
 //
 // Two launches:
 //  * q1_act_image_kernel converts x once into a ready-to-load A operand image
-//    (see q1_fp8.h for the split): per row block rb (8 activation rows) and
-//    group g a 2 KB tile in MFMA lane order, [lane][32 B] (bytes 0..15 =
-//    k-half 0, 16..31 = k-half 1); per (rb, span of 4 groups) one E8M0 scale
-//    dword per lane (byte g % 4); per (rb, g) 16 floats for the accumulator
-//    input (-X/2 or X on the hi rows, 0 on the lo rows).
-//  * q1_wide_kernel: a workgroup of 8 waves owns 8 row blocks (64 rows) and
+//    (see q1_fp8.h for the split x = hi + lo/16): per row block rb (16
+//    activation rows) and group g two 2 KB tiles (hi, lo) in MFMA lane order,
+//    [lane][32 B] (bytes 0..15 = k-half 0, 16..31 = k-half 1); per (rb, span
+//    of 4 groups) two E8M0 scale dwords per lane (hi, lo; byte g % 4); per
+//    (rb, g) 16 floats for the accumulator input (-X/2, or X for affine).
+//  * q1_wide_kernel: a workgroup of 8 waves owns 8 row blocks (128 rows) and
 //    TNB * 16 weight rows; wave w owns row block w and all TNB column blocks,
-//    so its A operand comes straight from the image (no sharing needed),
-//    while the weights of each span (4 groups) are staged once per
-//    workgroup in LDS as [row][word q][group] (80-byte rows: the staging
-//    writes and the 16-byte reads of lane (row, q) spread over the banks).
-//    Per span and column block a lane reads its words of the 4 groups and
-//    their 4 scales, expands each word with one AND per bit class and issues
-//    one MFMA per group; the group scale multiplies the result into the
-//    accumulator (and b * X for affine tensors).
+//    so its A operands come straight from the image, while the weights of
+//    each span (4 groups) are staged once per workgroup in LDS as [row][word
+//    q][group] (80-byte rows: the staging writes and the reads of lane
+//    (row, q) spread over the banks), with their scales (and biases) as fp32.
+//    Per half span (2 groups) and column block a lane reads its 2 words and
+//    scales, expands each word with one AND per bit class and chains two
+//    MFMAs per group through the accumulator input (hi, then lo with its own
+//    block scale), so the expansion and the group-scale multiply-add are paid
+//    once per 16 activation rows; b * X is added for affine tensors.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -36,6 +37,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float v2f_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
@@ -68,10 +70,10 @@ __global__ __launch_bounds__(256) void q1_act_image_kernel(const uint16_t* __res
   const int tid = threadIdx.x;
   const int b = tid & 3;
   const int g = (int)blockIdx.x * 64 + (tid >> 2);
-  const int64_t m = blockIdx.y;  // 0 .. 8*MB-1
-  const bool valid = g < G;
+  const int64_t m = blockIdx.y;  // 0 .. 16*MB-1
+  const int Gp = 4 * nspan;  // groups padded to whole spans (zero operands)
   uint32_t wd[16];
-  if (valid && m < M) {
+  if (g < G && m < M) {
     const u32x4* src = reinterpret_cast<const u32x4*>(x + m * x_ld + (int64_t)g * 128 + b * 32);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -89,27 +91,25 @@ __global__ __launch_bounds__(256) void q1_act_image_kernel(const uint16_t* __res
   q1_convert_word(wd, hi, lo, sc, X);
   X += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, X), 0xB1, 0xf, 0xf, false));
   X += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, X), 0x4E, 0xf, 0xf, false));
-  if (!valid) return;
-  const int64_t rb = m >> 3;
-  const int ml = (int)(m & 7);
-  // chunk (quarter qa = 2*(b & 1) + c, k-half b >> 1) holds in dword
-  // 2*(j & 1) + hh the class-j bytes of half word hh, j >> 1 == c
-  unsigned char* tile = img + ((rb * G + g) * 64) * 32 + (b >> 1) * 16;
+  if (g >= Gp) return;
+  const int64_t rb = m >> 4;
+  const int ml = (int)(m & 15);
+  // chunk (quarter qa = 2*(b & 1) + c, k-half b >> 1) of lane qa*16 + ml holds
+  // in dword 2*(j & 1) + hh the class-j bytes of half word hh, j >> 1 == c
+  unsigned char* tile = img + (rb * Gp + g) * 4096 + (b >> 1) * 16;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int qa = 2 * (b & 1) + c;
     *reinterpret_cast<u32x4*>(tile + (qa * 16 + ml) * 32) =
         u32x4{hi[2 * c][0], hi[2 * c][1], hi[2 * c + 1][0], hi[2 * c + 1][1]};
-    *reinterpret_cast<u32x4*>(tile + (qa * 16 + 8 + ml) * 32) =
+    *reinterpret_cast<u32x4*>(tile + 2048 + (qa * 16 + ml) * 32) =
         u32x4{lo[2 * c][0], lo[2 * c][1], lo[2 * c + 1][0], lo[2 * c + 1][1]};
   }
   // scale of A row r, 32-weight block j (= word b) sits in lane r + 16 j
-  unsigned char* sp = sc_img + ((rb * nspan + (g >> 2)) * 64) * 4 + (g & 3);
-  sp[(ml + 16 * b) * 4] = (unsigned char)(sc + 127);
-  sp[(8 + ml + 16 * b) * 4] = (unsigned char)(sc + 123);
-  float* xs = xs_img + (rb * G + g) * 16;
-  if (b == 0) xs[ml] = AFFINE ? X : -0.5f * X;
-  if (b == 1) xs[8 + ml] = 0.0f;
+  unsigned char* sp = sc_img + (rb * nspan + (g >> 2)) * 512 + (ml + 16 * b) * 4 + (g & 3);
+  sp[0] = (unsigned char)(sc + 127);
+  sp[256] = (unsigned char)(sc + 123);
+  if (b == 0) xs_img[(rb * Gp + g) * 16 + ml] = AFFINE ? X : -0.5f * X;
 }
 
 struct WideArgs {
@@ -142,13 +142,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kBufWord3);
 }
 
+// One group's two chained products for this lane: hi (accumulator input C)
+// then lo (accumulator input = the hi result), block scale byte BYTE of the
+// hi and lo scale dwords.
+template <int BYTE>
+__device__ __forceinline__ v4f mfma_hilo(const v8i& Ahi, const v8i& Alo, const v8i& B, const v4f& C, uint32_t shi,
+                                         uint32_t slo) {
+  const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Ahi, B, C, 0, 4, BYTE, (int)shi, 0, 0x7f7f7f7f);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Alo, B, d, 0, 4, BYTE, (int)slo, 0, 0x7f7f7f7f);
+}
+
 template <bool AFFINE, bool MBF16, int TNB>
 __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
   constexpr int ROWS = TNB * 16;                   // weight rows of the workgroup
   constexpr int LOADS = (ROWS * 4 + kThreads - 1) / kThreads;  // 16-byte staging loads per thread
+  static_assert(ROWS <= kThreads, "one thread per staged row for the scales");
   __shared__ __align__(16) unsigned char wsm[2][ROWS * kRowB];
-  __shared__ __align__(16) uint32_t ssm[2][ROWS * 2];  // 4 fp16/bf16 scales per row
-  __shared__ __align__(16) uint32_t bsm[AFFINE ? 2 : 1][AFFINE ? ROWS * 2 : 2];
+  __shared__ __align__(16) float ssm[2][ROWS * 4];  // the 4 group scales of each row, fp32
+  __shared__ __align__(16) float bsm[AFFINE ? 2 : 1][AFFINE ? ROWS * 4 : 4];
   __shared__ __align__(16) float xsm[2][kWaves * 4 * 16];  // group sums of a span: [row block][group][row]
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -184,10 +195,11 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
       const uint32_t off = ((uint32_t)n * row_bytes + (uint32_t)g * 16u) | (ok ? 0u : kOOB);
       wreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 2);
     }
-    {  // group sums: thread -> (row block, group, row)
+    {  // group sums: thread -> (row block, group, row); a row block past
+       // MB (its wave computes nothing) reads the last one's
       const int rbl = tid >> 6, g = 4 * sp + ((tid >> 4) & 3);
-      const int rbg = tm * kWaves + rbl;
-      xreg = (rbg < a.MB && g < a.G) ? a.xs_img[((int64_t)rbg * a.G + g) * 16 + (tid & 15)] : 0.0f;
+      const int rbg = min(tm * kWaves + rbl, a.MB - 1);
+      xreg = a.xs_img[((int64_t)rbg * (4 * a.nspan) + g) * 16 + (tid & 15)];
     }
     // scales (and biases) of groups 4sp..4sp+3, one row per thread
     const int row = tid;
@@ -220,139 +232,151 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
     }
     xsm[buf][tid] = xreg;
     if (tid < ROWS) {
-      ssm[buf][2 * tid] = sreg[0];
-      ssm[buf][2 * tid + 1] = sreg[1];
-      if (AFFINE) {
-        bsm[buf][2 * tid] = breg[0];
-        bsm[buf][2 * tid + 1] = breg[1];
-      }
+      *reinterpret_cast<v4f*>(&ssm[buf][4 * tid]) =
+          v4f{meta_val<MBF16>(sreg[0]), meta_val<MBF16>(sreg[0] >> 16), meta_val<MBF16>(sreg[1]),
+              meta_val<MBF16>(sreg[1] >> 16)};
+      if (AFFINE)
+        *reinterpret_cast<v4f*>(&bsm[buf][4 * tid]) =
+            v4f{meta_val<MBF16>(breg[0]), meta_val<MBF16>(breg[0] >> 16), meta_val<MBF16>(breg[1]),
+                meta_val<MBF16>(breg[1] >> 16)};
     }
   };
 
-  // ---- this wave's A operands for span sp (4 groups) ----
-  v8i A[4];
-  uint32_t scale_a = 0;
-  auto a_load = [&](int sp, v8i (&Ao)[4], uint32_t& so) {
+  // ---- this wave's A operands: half span h (groups 4sp+2h, 4sp+2h+1) ----
+  // A[e][0] = hi, A[e][1] = lo of group 4sp+2h+e
+  auto a_load = [&](int sp, int h, v8i (&Ao)[2][2]) {
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      const int g = 4 * sp + gi;
-      if (g < a.G) {  // (uniform)
-        const u32x4* t = reinterpret_cast<const u32x4*>(a.img + (((int64_t)rb * a.G + g) * 64 + lane) * 32);
+    for (int e = 0; e < 2; ++e) {
+      const int g = 4 * sp + 2 * h + e;  // (groups past G are zero in the image)
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl) {
+        const u32x4* t = reinterpret_cast<const u32x4*>(a.img + ((int64_t)rb * (4 * a.nspan) + g) * 4096 +
+                                                        hl * 2048 + lane * 32);
         const u32x4 h0 = t[0], h1 = t[1];
-        Ao[gi] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-      } else {
-        Ao[gi] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        Ao[e][hl] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
       }
     }
-    so = a.sc_img[((int64_t)rb * a.nspan + sp) * 64 + lane];
+  };
+  auto sc_load = [&](int sp, uint32_t& shi, uint32_t& slo) {
+    const uint32_t* t = a.sc_img + ((int64_t)rb * a.nspan + sp) * 128 + lane;
+    shi = t[0];
+    slo = t[64];
   };
 
   v4f acc[TNB];
 #pragma unroll
   for (int j = 0; j < TNB; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // ---- products of half span h from LDS buffer buf ----
+  auto compute = [&](int buf, int h, const v8i (&A)[2][2], uint32_t shi, uint32_t slo) {
+    // groups past G (last span) have zero A operands, zero weights and zero
+    // scales, so every span runs all its groups without branches
+    v4f XS[2];  // this wave's group sums, rows 4q..4q+3
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      XS[e] = reinterpret_cast<const v4f*>(&xsm[buf][(wave * 4 + 2 * h + e) * 16])[q];
+    // the LDS reads of column block j+1 are issued before block j's work
+    auto rd_w = [&](int j) { return *reinterpret_cast<const u32x2*>(wsm[buf] + (j * 16 + nl) * kRowB + q * 16 + 8 * h); };
+    auto rd_s = [&](int j) { return *reinterpret_cast<const v2f_t*>(&ssm[buf][4 * (j * 16 + nl) + 2 * h]); };
+    auto rd_b = [&](int j) {
+      return AFFINE ? *reinterpret_cast<const v2f_t*>(&bsm[buf][4 * (j * 16 + nl) + 2 * h]) : v2f_t{0.f, 0.f};
+    };
+    auto fma_block = [&](int j, const v4f (&Dv)[2], v2f_t sv, v2f_t bv) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(sv[e], Dv[e][i], acc[j][i]);
+        if (AFFINE) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(bv[e], XS[e][i], acc[j][i]);
+        }
+      }
+    };
+    u32x2 w2n = rd_w(0);
+    v2f_t s2n = rd_s(0), b2n = rd_b(0);
+    v4f Dp[2];
+    v2f_t s2p = {0.f, 0.f}, b2p = {0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < TNB; ++j) {
+      const u32x2 w2 = w2n;
+      const v2f_t s2 = s2n, b2 = b2n;
+      if (j + 1 < TNB) {
+        w2n = rd_w(j + 1);
+        s2n = rd_s(j + 1);
+        b2n = rd_b(j + 1);
+      }
+      v4f D[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        int Bv[8];
+        q1_expand_b(w2[e], Bv);
+        const v8i B = {Bv[0], Bv[1], Bv[2], Bv[3], 0, 0, 0, 0};
+        const v4f C = AFFINE ? v4f{0.f, 0.f, 0.f, 0.f} : XS[e];
+        if (h == 0 && e == 0) D[e] = mfma_hilo<0>(A[e][0], A[e][1], B, C, shi, slo);
+        else if (h == 0) D[e] = mfma_hilo<1>(A[e][0], A[e][1], B, C, shi, slo);
+        else if (e == 0) D[e] = mfma_hilo<2>(A[e][0], A[e][1], B, C, shi, slo);
+        else D[e] = mfma_hilo<3>(A[e][0], A[e][1], B, C, shi, slo);
+      }
+      // the scale multiply-adds of block j-1 go after block j's products,
+      // so they never wait for a product just issued
+      if (j > 0) fma_block(j - 1, Dp, s2p, b2p);
+      Dp[0] = D[0];
+      Dp[1] = D[1];
+      s2p = s2;
+      b2p = b2;
+      // keep later blocks' LDS reads from being hoisted (their results would
+      // all be live at once)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    fma_block(TNB - 1, Dp, s2p, b2p);
+  };
+
+  // A0 holds the first half span's operands, A1 the second's; each loads
+  // while the other half computes (no register copies between spans)
+  v8i A0[2][2], A1[2][2];
+  uint32_t shi = 0, slo = 0, shn = 0, sln = 0;
   stage_load(0);
-  if (live) a_load(0, A, scale_a);
+  if (live) {
+    a_load(0, 0, A0);
+    sc_load(0, shi, slo);
+  }
   stage_store(0);
   lds_barrier();
 
   for (int sp = 0; sp < a.nspan; ++sp) {
     const int buf = sp & 1;
-    v8i An[4];
-    uint32_t sn = 0;
-    if (sp + 1 < a.nspan) {
-      stage_load(sp + 1);
-      if (live) a_load(sp + 1, An, sn);
-    }
+    const bool more = sp + 1 < a.nspan;
+    if (more) stage_load(sp + 1);
     if (live) {
-      // groups past G (last span) have zero A operands, zero weights and zero
-      // scales, so every span runs all 4 groups without branches
-      // the LDS reads of column block j+1 are issued before block j's work
-      auto rd_w = [&](int j) { return *reinterpret_cast<const u32x4*>(wsm[buf] + (j * 16 + nl) * kRowB + q * 16); };
-      auto rd_s = [&](int j) { return *reinterpret_cast<const u32x2*>(&ssm[buf][2 * (j * 16 + nl)]); };
-      auto rd_b = [&](int j) {
-        return AFFINE ? *reinterpret_cast<const u32x2*>(&bsm[buf][2 * (j * 16 + nl)]) : u32x2{0u, 0u};
-      };
-      v4f XS[4];  // this wave's group sums of the span, rows 4q..4q+3
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) XS[gi] = reinterpret_cast<const v4f*>(&xsm[buf][(wave * 4 + gi) * 16])[q];
-      v4f Dp[4];
-      u32x2 s4p = {0u, 0u}, b4p = {0u, 0u};
-      auto fma_block = [&](int j, const v4f (&Dv)[4], u32x2 sv4, u32x2 bv4) {
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const float sv = meta_val<MBF16>(sv4[gi >> 1] >> (16 * (gi & 1)));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(sv, Dv[gi][i], acc[j][i]);
-          if (AFFINE) {
-            const float bv = meta_val<MBF16>(bv4[gi >> 1] >> (16 * (gi & 1)));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(bv, XS[gi][i], acc[j][i]);
-          }
-        }
-      };
-      u32x4 w4n = rd_w(0);  // word q of groups 0..3
-      u32x2 s4n = rd_s(0), b4n = rd_b(0);
-#pragma unroll
-      for (int j = 0; j < TNB; ++j) {
-        const u32x4 w4 = w4n;
-        const u32x2 s4 = s4n, b4 = b4n;
-        if (j + 1 < TNB) {
-          w4n = rd_w(j + 1);
-          s4n = rd_s(j + 1);
-          b4n = rd_b(j + 1);
-        }
-        v4f D[4];
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          int Bv[8];
-          q1_expand_b(w4[gi], Bv);
-          const v8i B = {Bv[0], Bv[1], Bv[2], Bv[3], 0, 0, 0, 0};
-          const v4f C = AFFINE ? v4f{0.f, 0.f, 0.f, 0.f} : XS[gi];
-          if (gi == 0)
-            D[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, C, 0, 4, 0, (int)scale_a, 0, 0x7f7f7f7f);
-          else if (gi == 1)
-            D[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, C, 0, 4, 1, (int)scale_a, 0, 0x7f7f7f7f);
-          else if (gi == 2)
-            D[2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, C, 0, 4, 2, (int)scale_a, 0, 0x7f7f7f7f);
-          else
-            D[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[3], B, C, 0, 4, 3, (int)scale_a, 0, 0x7f7f7f7f);
-        }
-        // the scale multiply-adds of block j-1 go after block j's products,
-        // so they never wait for a product just issued
-        if (j > 0) fma_block(j - 1, Dp, s4p, b4p);
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) Dp[gi] = D[gi];
-        s4p = s4;
-        b4p = b4;
+      a_load(sp, 1, A1);
+      compute(buf, 0, A0, shi, slo);
+      // (the next loads must not move above the products that read A0)
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const int spn = more ? sp + 1 : 0;
+        a_load(spn, 0, A0);
+        sc_load(spn, shn, sln);
       }
-      fma_block(TNB - 1, Dp, s4p, b4p);
+      compute(buf, 1, A1, shi, slo);
+      shi = shn;
+      slo = sln;
     }
-    if (sp + 1 < a.nspan) stage_store(buf ^ 1);  // that buffer was last read before the previous barrier
+    if (more) stage_store(buf ^ 1);  // that buffer was last read before the previous barrier
     lds_barrier();
-    if (sp + 1 < a.nspan && live) {
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        A[gi] = An[gi];
-      }
-      scale_a = sn;
-    }
   }
 
   if (!live) return;
-  // lane l of half ab: activation row 4*((l>>4)&1) + 2*ab + (l>>5) of the row
-  // block (hi + lo added), weight row l & 15 of the column block
+  // lane l: activation rows 16 rb + 4 (l >> 4) + i, weight row l & 15 of each
+  // column block
+  const int64_t m0 = (int64_t)rb * 16 + 4 * q;
 #pragma unroll
   for (int j = 0; j < TNB; ++j) {
-    auto p01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[j][0]), __float_as_uint(acc[j][1]), false, false);
-    auto p23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[j][2]), __float_as_uint(acc[j][3]), false, false);
-    const float v0 = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
-    const float v1 = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
     const int64_t n = n0 + j * 16 + nl;
-    const int64_t mA = (int64_t)rb * 8 + 4 * ((lane >> 4) & 1) + (lane >> 5);
     if (n < a.N) {
-      if (mA < a.M) store_out(a.out, a.out_dtype, mA * a.out_ld + n, v0);
-      if (mA + 2 < a.M) store_out(a.out, a.out_dtype, (mA + 2) * a.out_ld + n, v1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (m0 + i < a.M) store_out(a.out, a.out_dtype, (m0 + i) * a.out_ld + n, acc[j][i]);
     }
   }
 }
@@ -386,7 +410,7 @@ bool plan_wide(int64_t M, int64_t N, int64_t K, bool affine, WidePlan* p, const 
   p->K = (int)K;
   p->G = (int)(K / 128);
   p->nspan = (p->G + 3) / 4;
-  p->MB = (int)((M + 7) / 8);
+  p->MB = (int)((M + 15) / 16);
   p->mtiles = (p->MB + kWaves - 1) / kWaves;
   // column blocks per workgroup: the choice that keeps the most CUs busy in
   // the last round of workgroups (ties: the wider tile)
@@ -395,7 +419,6 @@ bool plan_wide(int64_t M, int64_t N, int64_t K, bool affine, WidePlan* p, const 
   const int cand[3] = {17, 16, 10};
   double best = -1.0;
   for (int tnb : cand) {
-    if (affine && tnb == 17) continue;  // (its bias registers would spill)
     const int64_t ntn = (nbk + tnb - 1) / tnb;
     const int64_t wgs = ntn * p->mtiles;
     const double eff = (double)wgs / (double)(((wgs + cus - 1) / cus) * cus);
@@ -406,9 +429,9 @@ bool plan_wide(int64_t M, int64_t N, int64_t K, bool affine, WidePlan* p, const 
       p->wgs = wgs;
     }
   }
-  const size_t img = (size_t)p->MB * p->G * 2048;
-  const size_t sc = (size_t)p->MB * p->nspan * 256;
-  const size_t xs = (size_t)p->MB * p->G * 64;
+  const size_t img = (size_t)p->MB * p->nspan * 4 * 4096;
+  const size_t sc = (size_t)p->MB * p->nspan * 512;
+  const size_t xs = (size_t)p->MB * p->nspan * 4 * 64;
   p->sc_off = (img + 255) / 256 * 256;
   p->xs_off = p->sc_off + (sc + 255) / 256 * 256;
   p->ws_bytes = p->xs_off + (xs + 255) / 256 * 256;
@@ -420,7 +443,7 @@ hipError_t launch_wide(const WidePlan& p, const uint16_t* x, int64_t x_ld, const
   unsigned char* img = ws;
   unsigned char* sc = ws + p.sc_off;
   float* xs = reinterpret_cast<float*>(ws + p.xs_off);
-  const dim3 ig((unsigned)((p.G + 63) / 64), (unsigned)(p.MB * 8));
+  const dim3 ig((unsigned)((4 * p.nspan + 63) / 64), (unsigned)(p.MB * 16));
   if (w.symmetric)
     hipLaunchKernelGGL((q1_act_image_kernel<false>), ig, dim3(256), 0, s, x, x_ld, p.M, p.G, p.nspan, img, sc, xs);
   else
