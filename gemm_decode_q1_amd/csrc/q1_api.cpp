@@ -131,12 +131,13 @@ int packed_kernel_env() {
 
 // More than 8 rows: the wide matrix-core kernel straight from the packed
 // weights; Q1_WIDE_KERNEL=dequant selects the dequantise-to-bf16 + GEMM path.
+// Q1_WIDE_KERNEL=dequant selects the dense fallback (dequantise to bf16, then
+// the bf16 GEMM) for M > max rows; read on every call, so a caller can switch
+// between the two wide paths (the workspace query must see the same setting
+// as the call it sizes).
 bool use_wide_kernel() {
-  static const bool v = [] {
-    const char* e = getenv("Q1_WIDE_KERNEL");
-    return !(e && strcmp(e, "dequant") == 0);
-  }();
-  return v;
+  const char* e = getenv("Q1_WIDE_KERNEL");
+  return !(e && strcmp(e, "dequant") == 0);
 }
 
 struct PackedPlan {

@@ -175,7 +175,9 @@ _need_cache = {}
 
 
 def _qmm_need(L, M: int, w: PackedQ1, d: _Weight) -> int:
-    key = (M, w.N, w.K, d.meta_dtype, d.symmetric)
+    # (the wide-path choice follows Q1_WIDE_KERNEL, which the library reads
+    # on every call, so it is part of the key)
+    key = (M, w.N, w.K, d.meta_dtype, d.symmetric, os.environ.get("Q1_WIDE_KERNEL"))
     n = _need_cache.get(key)
     if n is None:
         n = L.q1_qmm_workspace_bytes(M, ctypes.byref(d))
