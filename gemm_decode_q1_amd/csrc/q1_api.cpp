@@ -449,7 +449,10 @@ q1_status q1_ffn(const void* x, int64_t M, const q1_weight* gate, const q1_weigh
   if (L.wide_mma) {  // the operand image region is reused by the three products in turn
     unsigned char* img = ws + L.deq_off;
     hipError_t e = q1::launch_wide(L.wg, xb, H, g, gf, q1::F32, I, img, s);
-    if (e == hipSuccess) e = q1::launch_wide(L.wu, xb, H, u, uf, q1::F32, I, img, s);
+    // gate and up read the same x: one image serves both when their
+    // accumulator terms agree (both symmetric or both affine)
+    if (e == hipSuccess)
+      e = q1::launch_wide(L.wu, xb, H, u, uf, q1::F32, I, img, s, g.symmetric != u.symmetric);
     if (e == hipSuccess) e = q1::launch_silu_mul(gf, uf, h, M * I, s);
     if (e == hipSuccess) e = q1::launch_wide(L.wd, h, I, d, y, q1::BF16, Ho, img, s);
     return hip_status(e, "wide FFN launch");

@@ -162,8 +162,11 @@ struct WidePlan {
 };
 
 bool plan_wide(int64_t M, int64_t N, int64_t K, bool affine, WidePlan* plan, const char** why);
+// make_image = false reuses the image already in ws (same x, same K, same
+// symmetric/affine kind: the group-sum terms differ between the two kinds).
 hipError_t launch_wide(const WidePlan& plan, const uint16_t* x, int64_t x_ld, const QMat& w, void* out,
-                       int32_t out_dtype, int64_t out_ld, unsigned char* ws, hipStream_t stream);
+                       int32_t out_dtype, int64_t out_ld, unsigned char* ws, hipStream_t stream,
+                       bool make_image = true);
 
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* B, int64_t M, int64_t N, int64_t K, void* y,
                             int32_t y_dtype, hipStream_t stream);

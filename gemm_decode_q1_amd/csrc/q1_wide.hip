@@ -439,17 +439,19 @@ bool plan_wide(int64_t M, int64_t N, int64_t K, bool affine, WidePlan* p, const 
 }
 
 hipError_t launch_wide(const WidePlan& p, const uint16_t* x, int64_t x_ld, const QMat& w, void* out, int32_t out_dtype,
-                       int64_t out_ld, unsigned char* ws, hipStream_t s) {
+                       int64_t out_ld, unsigned char* ws, hipStream_t s, bool make_image) {
   unsigned char* img = ws;
   unsigned char* sc = ws + p.sc_off;
   float* xs = reinterpret_cast<float*>(ws + p.xs_off);
-  const dim3 ig((unsigned)((4 * p.nspan + 63) / 64), (unsigned)(p.MB * 16));
-  if (w.symmetric)
-    hipLaunchKernelGGL((q1_act_image_kernel<false>), ig, dim3(256), 0, s, x, x_ld, p.M, p.G, p.nspan, img, sc, xs);
-  else
-    hipLaunchKernelGGL((q1_act_image_kernel<true>), ig, dim3(256), 0, s, x, x_ld, p.M, p.G, p.nspan, img, sc, xs);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (make_image) {
+    const dim3 ig((unsigned)((4 * p.nspan + 63) / 64), (unsigned)(p.MB * 16));
+    if (w.symmetric)
+      hipLaunchKernelGGL((q1_act_image_kernel<false>), ig, dim3(256), 0, s, x, x_ld, p.M, p.G, p.nspan, img, sc, xs);
+    else
+      hipLaunchKernelGGL((q1_act_image_kernel<true>), ig, dim3(256), 0, s, x, x_ld, p.M, p.G, p.nspan, img, sc, xs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   WideArgs g;
   g.packed = w.packed;
   g.scales = w.scales;

@@ -407,14 +407,19 @@ def test_ffn_dense_fallback_small():
     _ffn_check(5, True, 24, "dense", dense=True)
 
 
-def test_ffn_unfused_when_formats_differ():
-    _say("ffn unfused (gate f16 sym, up bf16 affine)")
-    rng = np.random.Generator(np.random.PCG64(55))
+@pytest.mark.parametrize("M,up_sym", [(3, False), (20, False), (20, True), (33, None)])
+def test_ffn_mixed_formats(M, up_sym):
+    """Gate f16 symmetric with up bf16 affine (the narrow path cannot pair
+    them; the wide path converts x once per kind), up of the gate's kind (one
+    activation image for both), and all three affine (up_sym None)."""
+    _say(f"ffn mixed formats M={M} up_sym={up_sym}")
+    rng = np.random.Generator(np.random.PCG64(55 + M))
     H, I, Ho = 1024, 640, 384
-    g = S.draw_weight(rng, I, H, "f16", True)
-    u = S.draw_weight(rng, I, H, "bf16", False)
+    gsym = up_sym is not None
+    g = S.draw_weight(rng, I, H, "f16" if gsym else "bf16", gsym)
+    u = S.draw_weight(rng, I, H, "f16" if up_sym else "bf16", bool(up_sym))
     d = S.draw_weight(rng, Ho, I, "bf16", False)
-    x = S.draw_x(rng, 3, H)
+    x = S.draw_x(rng, M, H)
     y, h = Q.q1_ffn(x_dev(x), *(Q.PackedQ1.from_host(t) for t in (g, u, d)), return_hidden=True)
     ref = O.ffn_ref(x, wdict(g), wdict(u), wdict(d))
     dh = np.abs(O.bf16_to_f32(out_host(h)).astype(np.float64) - ref["h64"])
