@@ -11,8 +11,8 @@
 // sc = frexp(max |x|) - 7, so |x| * 2^-sc < 2^7 and at most 2^8 after the
 // class factor, below fp8's largest value (448).  hi carries the top 4 of a
 // bf16's 8 significant bits (rounded), lo the rest, so the pair is exact for
-// every value within 2^12 of the word's largest magnitude; below that the
-// error is at most 2^-19 of it.
+// every value within a factor 2^11 of the word's largest magnitude (lo then
+// stays on fp8's grid); below that the error is at most 2^-19 of it.
 #pragma once
 
 #include <hip/hip_runtime.h>
