@@ -244,13 +244,16 @@ bool plan_gemv(int M, int64_t N, int64_t K, bool pair, bool affine, GemvPlan* p,
   }
   p->lds_bytes = (size_t)gemv_lds_bytes(M);
   p->threads = gemv_threads(M);
+  // Workgroups: as many as are resident at once (one or two per CU, by LDS),
+  // the units split evenly over them (an even count each, so gate/up pairs
+  // never straddle two workgroups).  A second round of workgroups on a few
+  // CUs would double those CUs' work, so the count never exceeds the slots.
   const int per_cu = (int)((160 * 1024) / p->lds_bytes) >= 2 ? 2 : 1;
-  const int64_t target = (int64_t)device_cus() * per_cu;
-  const int64_t wx = (target + p->KS - 1) / p->KS;
+  const int64_t slots = (int64_t)device_cus() * per_cu;
+  const int64_t wx = slots / p->KS > 0 ? slots / p->KS : 1;
   int64_t upw = (p->units + wx - 1) / wx;
-  const int64_t waves = p->threads / 64;
-  upw = (upw + 2 * waves - 1) / (2 * waves) * (2 * waves);
-  if (upw < 2 * waves) upw = 2 * waves;
+  upw += upw & 1;
+  if (upw < 2) upw = 2;
   p->units_per_wg = upw;
   p->wgs_x = (int)((p->units + upw - 1) / upw);
   p->partial_floats = (p->KS > 1) ? (size_t)p->KS * M * p->units : 0;
