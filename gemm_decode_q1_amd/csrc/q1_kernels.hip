@@ -26,57 +26,105 @@
 namespace q1 {
 
 // ---------------------------------------------------------------------------
-// Dequantisation / row gather.  One thread writes 8 consecutive outputs of a
-// row (16 bytes for 16-bit outputs), so a wave stores 1 KB contiguous.  Per
-// group only two values exist: v0 = fl(fl(s*0) + b) and v1 = fl(s + b); they
-// are rounded once and selected by the bits.
+// Dequantisation / row gather.  A piece is 8 consecutive outputs of a row (16
+// bytes for 16-bit outputs), so a wave stores 1 KB contiguous.  Per group only
+// two values exist: v0 = fl(fl(s*0) + b) and v1 = fl(s + b); they are rounded
+// once and selected by the bits.  A thread takes kDqU pieces, stride apart,
+// and issues all their loads (ids first, then words and metadata) before any
+// store, so the id -> word -> store chain of one piece overlaps the others'.
+// The row of piece t is t / per_row by a multiply-high and shift (DivMagic,
+// exact for every 32-bit t; the launch keeps T * per_row below 2^32).
 // ---------------------------------------------------------------------------
+
+constexpr int kDqU = 4;
+
+// q = floor(t / d) = (umulhi(t, m) + t) >> l for 0 <= t < 2^32, with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1 (round-up method).
+struct DivMagic {
+  uint32_t m, l;
+};
+
+static DivMagic div_magic(uint32_t d) {
+  uint32_t l = 0;
+  while (((uint64_t)1 << l) < d) ++l;
+  const uint64_t m = ((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d) + 1;
+  return DivMagic{(uint32_t)m, l};
+}
+
+__device__ __forceinline__ uint32_t div_by(uint32_t t, DivMagic dm) {
+  return (uint32_t)(((uint64_t)__umulhi(t, dm.m) + t) >> dm.l);
+}
 
 template <int OUT, bool MBF16>
 __global__ __launch_bounds__(256) void q1_dequant_kernel(const uint32_t* __restrict__ packed,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint16_t* __restrict__ biases, int symmetric,
                                                          int64_t nrows, int64_t K, const void* __restrict__ ids,
-                                                         int ids64, int64_t T, void* __restrict__ out) {
-  const int64_t per_row = K >> 3;
-  const int64_t total = T * per_row;
+                                                         int ids64, uint32_t total, DivMagic per_row_div,
+                                                         void* __restrict__ out) {
+  const uint32_t per_row = (uint32_t)(K >> 3);
   const int64_t wpr = K >> 5, gpr = K >> 7;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-    const int64_t r = t / per_row;
-    const int64_t piece = t - r * per_row;
-    int64_t row = r;
-    if (ids != nullptr) row = ids64 ? static_cast<const int64_t*>(ids)[r] : (int64_t) static_cast<const int32_t*>(ids)[r];
-    uint32_t bits = 0;
-    float v0 = 0.0f, v1 = 0.0f;
-    if (row >= 0 && row < nrows) {
-      const uint32_t word = packed[row * wpr + (piece >> 2)];
-      bits = (word >> (8 * (int)(piece & 3))) & 0xffu;
-      const int64_t g = row * gpr + (piece >> 4);
-      const float s = meta_to_f32<MBF16>(scales[g]);
-      const float b = symmetric ? -0.5f * s : meta_to_f32<MBF16>(biases[g]);
-      v0 = __builtin_fmaf(s, 0.0f, b);
-      v1 = __builtin_fmaf(s, 1.0f, b);
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t t0 = blockIdx.x * blockDim.x + threadIdx.x; t0 < total; t0 += kDqU * stride) {
+    uint32_t r[kDqU], piece[kDqU];
+    int64_t row[kDqU];
+    bool ok[kDqU];
+#pragma unroll
+    for (int u = 0; u < kDqU; ++u) {
+      const uint32_t t = t0 + (uint32_t)u * stride;  // < 2^32: total + kDqU * stride fits (launch)
+      r[u] = div_by(t, per_row_div);
+      piece[u] = t - r[u] * per_row;
+      row[u] = r[u];
+      if (ids != nullptr && t < total)
+        row[u] = ids64 ? static_cast<const int64_t*>(ids)[r[u]] : (int64_t) static_cast<const int32_t*>(ids)[r[u]];
     }
-    const int64_t o = r * K + piece * 8;
-    if (OUT == F32) {
-      float vals[8];
+    uint32_t word[kDqU], sb[kDqU], bb[kDqU];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vals[j] = ((bits >> j) & 1u) ? v1 : v0;
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + o);
-      dst[0] = make_float4(vals[0], vals[1], vals[2], vals[3]);
-      dst[1] = make_float4(vals[4], vals[5], vals[6], vals[7]);
-    } else {
-      const uint32_t o0 = (OUT == BF16) ? f32_to_bf16_bits(v0) : f32_to_f16_bits(v0);
-      const uint32_t o1 = (OUT == BF16) ? f32_to_bf16_bits(v1) : f32_to_f16_bits(v1);
-      uint32_t d[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = ((bits >> (2 * j)) & 1u) ? o1 : o0;
-        const uint32_t hi = ((bits >> (2 * j + 1)) & 1u) ? o1 : o0;
-        d[j] = lo | (hi << 16);
+    for (int u = 0; u < kDqU; ++u) {
+      const uint32_t t = t0 + (uint32_t)u * stride;
+      ok[u] = t < total && row[u] >= 0 && row[u] < nrows;
+      word[u] = 0u;
+      sb[u] = 0u;
+      bb[u] = 0u;
+      if (ok[u]) {
+        const int64_t g = row[u] * gpr + (piece[u] >> 4);
+        word[u] = packed[row[u] * wpr + (piece[u] >> 2)];
+        sb[u] = scales[g];
+        if (!symmetric) bb[u] = biases[g];
       }
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o) = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+#pragma unroll
+    for (int u = 0; u < kDqU; ++u) {
+      const uint32_t t = t0 + (uint32_t)u * stride;
+      if (t >= total) continue;
+      const uint32_t bits = ok[u] ? (word[u] >> (8 * (piece[u] & 3u))) & 0xffu : 0u;
+      float v0 = 0.0f, v1 = 0.0f;
+      if (ok[u]) {
+        const float s = meta_to_f32<MBF16>(sb[u]);
+        const float b = symmetric ? -0.5f * s : meta_to_f32<MBF16>(bb[u]);
+        v0 = __builtin_fmaf(s, 0.0f, b);
+        v1 = __builtin_fmaf(s, 1.0f, b);
+      }
+      const int64_t o = (int64_t)r[u] * K + (int64_t)piece[u] * 8;
+      if (OUT == F32) {
+        float vals[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vals[j] = ((bits >> j) & 1u) ? v1 : v0;
+        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + o);
+        dst[0] = make_float4(vals[0], vals[1], vals[2], vals[3]);
+        dst[1] = make_float4(vals[4], vals[5], vals[6], vals[7]);
+      } else {
+        const uint32_t o0 = (OUT == BF16) ? f32_to_bf16_bits(v0) : f32_to_f16_bits(v0);
+        const uint32_t o1 = (OUT == BF16) ? f32_to_bf16_bits(v1) : f32_to_f16_bits(v1);
+        uint32_t d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = ((bits >> (2 * j)) & 1u) ? o1 : o0;
+          const uint32_t hi = ((bits >> (2 * j + 1)) & 1u) ? o1 : o0;
+          d[j] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o) = make_uint4(d[0], d[1], d[2], d[3]);
+      }
     }
   }
 }
@@ -341,26 +389,44 @@ hipError_t launch_gemv(const GemvPlan& plan, const uint16_t* x, int64_t x_ld, co
 
 hipError_t launch_dequant(const QMat& w, const void* ids, int ids_int64, int64_t T, void* out, int32_t out_dtype,
                           hipStream_t stream) {
-  const int64_t total = T * (w.K >> 3);
-  if (total == 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
-  const int64_t cap = (int64_t)device_cus() * 16;
-  if (blocks > cap) blocks = cap;
+  const int64_t per_row = w.K >> 3;
+  if (T == 0 || per_row == 0) return hipSuccess;
+  const DivMagic dm = div_magic((uint32_t)per_row);
   const int sym = w.symmetric ? 1 : 0;
-#define Q1_DQ(OUT, MB)                                                                                              \
-  hipLaunchKernelGGL((q1_dequant_kernel<OUT, MB>), dim3((unsigned)blocks), dim3(256), 0, stream, w.packed, w.scales, \
-                     w.biases, sym, w.N, w.K, ids, ids_int64, T, out)
-  if (w.meta_bf16) {
-    if (out_dtype == F32) Q1_DQ(F32, true);
-    else if (out_dtype == F16) Q1_DQ(F16, true);
-    else Q1_DQ(BF16, true);
-  } else {
-    if (out_dtype == F32) Q1_DQ(F32, false);
-    else if (out_dtype == F16) Q1_DQ(F16, false);
-    else Q1_DQ(BF16, false);
-  }
+  const size_t osz = out_dtype == F32 ? 4 : 2;
+  // Rows in launches of at most 2^31 pieces, so piece indices (and the
+  // strided indices of a thread's last round) stay below 2^32.
+  const int64_t rows_per_launch = ((int64_t)1 << 31) / per_row;
+  for (int64_t r0 = 0; r0 < T; r0 += rows_per_launch) {
+    const int64_t tr = (T - r0 < rows_per_launch) ? T - r0 : rows_per_launch;
+    const uint32_t total = (uint32_t)(tr * per_row);
+    int64_t blocks = ((int64_t)total + 256 * kDqU - 1) / (256 * kDqU);
+    const int64_t cap = (int64_t)device_cus() * 16;
+    if (blocks > cap) blocks = cap;
+    const void* ids_c = ids == nullptr ? nullptr
+                                       : static_cast<const char*>(ids) + r0 * (ids_int64 ? 8 : 4);
+    const uint32_t* pk = ids == nullptr ? w.packed + r0 * (w.K >> 5) : w.packed;
+    const uint16_t* sc = ids == nullptr ? w.scales + r0 * (w.K >> 7) : w.scales;
+    const uint16_t* bi = (ids == nullptr && w.biases != nullptr) ? w.biases + r0 * (w.K >> 7) : w.biases;
+    const int64_t nrows = ids == nullptr ? tr : w.N;
+    void* o = static_cast<char*>(out) + (size_t)r0 * (size_t)w.K * osz;
+#define Q1_DQ(OUT, MB)                                                                                             \
+  hipLaunchKernelGGL((q1_dequant_kernel<OUT, MB>), dim3((unsigned)blocks), dim3(256), 0, stream, pk, sc, bi, sym, \
+                     nrows, w.K, ids_c, ids_int64, total, dm, o)
+    if (w.meta_bf16) {
+      if (out_dtype == F32) Q1_DQ(F32, true);
+      else if (out_dtype == F16) Q1_DQ(F16, true);
+      else Q1_DQ(BF16, true);
+    } else {
+      if (out_dtype == F32) Q1_DQ(F32, false);
+      else if (out_dtype == F16) Q1_DQ(F16, false);
+      else Q1_DQ(BF16, false);
+    }
 #undef Q1_DQ
-  return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* B, int64_t M, int64_t N, int64_t K, void* y,
