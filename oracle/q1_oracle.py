@@ -315,3 +315,60 @@ def ffn_y_bound(ref: dict, down: dict, weights_bf16: bool = False) -> np.ndarray
     lead = dh.shape[:-1]
     prop = dh.reshape(-1, dh.shape[-1]) @ wd.T
     return tolerance(ref["Ad"]) + prop.reshape(*lead, wd.shape[0])
+
+
+# --------------------------------------------------------------------------
+# Metadata: symmetric-bias check and sign packer
+# --------------------------------------------------------------------------
+
+
+def symmetric_mismatches(scales: np.ndarray, biases: np.ndarray, meta: str) -> int:
+    """Groups of an affine tensor whose stored bias cannot be replaced by the
+    derived ``-scale/2`` (Higgs PR #212, "What": validate symmetric Q1
+    metadata; "Walkthrough": loaders compact exact symmetric biases).
+
+    A group matches when scale and bias are finite and each code dequantises to
+    the same float32 value (bit for bit) with the stored bias as with
+    ``-0.5 * scale`` -- the literal formula of :func:`dequant_f32` taken both
+    ways.  Returns the number of groups that do not match."""
+    s = meta_to_f32(scales, meta)
+    b = meta_to_f32(biases, meta)
+    d = (np.float32(-0.5) * s).astype(np.float32)
+    same = np.isfinite(s) & np.isfinite(b)
+    with np.errstate(over="ignore", invalid="ignore"):
+        for code in (0.0, 1.0):
+            prod = (s * np.float32(code)).astype(np.float32)
+            with_bias = (prod + b).astype(np.float32)
+            derived = (prod + d).astype(np.float32)
+            same &= with_bias.view(np.uint32) == derived.view(np.uint32)
+    return int((~same).sum())
+
+
+def pack_signs(dense_bits: np.ndarray, dense: str, meta: str):
+    """Dense ``[N, K]`` bf16/f16 weights -> a symmetric packed tensor (Cactus
+    PR #775, commit notes: groups holding exactly {-s, +s} repack to sign bits
+    with zero error; rMLX issue #207: bit 0 -> -s_g, bit 1 -> +s_g, 32 weights
+    per word LSB first).
+
+    Per group of 128 weights: ``scale = round_meta(2 * max|w|)`` (NaNs left
+    out of the maximum), ``bit = (w > 0)``.  The group is exact when
+    dequantising the result to the dense dtype gives back every weight's bit
+    pattern and the group holds no NaN.  Returns ``(packed uint32 [N, K/32],
+    scales uint16 bits [N, K/128], number of inexact groups)``."""
+    dense_bits = np.asarray(dense_bits, dtype=np.uint16)
+    N, K = dense_bits.shape
+    G = K // GROUP
+    w = meta_to_f32(dense_bits, dense)              # the same decoders serve both 16-bit types
+    mag = np.abs(w).reshape(N, G, GROUP)
+    has_nan = np.isnan(mag).any(axis=2)
+    amax = np.fmax.reduce(mag, axis=2, initial=np.float32(0.0)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        scale_bits = round_to((np.float32(2.0) * amax).astype(np.float32), meta)
+    bits = (w > 0).astype(np.uint32)                # NaN > 0 is False
+    packed = np.zeros((N, K // 32), dtype=np.uint32)
+    for i in range(32):                             # weight 32j + i -> bit i of word j
+        packed |= bits[:, i::32] << np.uint32(i)
+    with np.errstate(invalid="ignore"):
+        back = dequantize(packed, scale_bits, None, meta, True, K, dense)
+    exact = (back.reshape(N, G, GROUP) == dense_bits.reshape(N, G, GROUP)).all(axis=2) & ~has_nan
+    return packed, scale_bits, int((~exact).sum())
