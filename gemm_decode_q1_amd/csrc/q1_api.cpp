@@ -389,6 +389,41 @@ q1_status q1_embed_rows(const void* ids, int32_t ids_are_int64, int64_t T, const
       "gather launch");
 }
 
+q1_status q1_check_symmetric(const q1_weight* w, uint32_t* count, void* stream) {
+  q1_status st = check_weight(w, "w");
+  if (st != Q1_OK) return st;
+  if (w->symmetric) return fail(Q1_ERR_INVALID_ARG, "w: already symmetric (no biases to check)");
+  if (count == nullptr || !aligned(count, 4)) return fail(Q1_ERR_INVALID_ARG, "count must be a 4-byte aligned device pointer");
+  st = check_current_device();
+  if (st != Q1_OK) return st;
+  return hip_status(q1::launch_symcheck(static_cast<const uint16_t*>(w->scales), static_cast<const uint16_t*>(w->biases),
+                                        w->N * (w->K / 128), w->meta_dtype == Q1_BF16, count,
+                                        static_cast<hipStream_t>(stream)),
+                    "symmetric check launch");
+}
+
+q1_status q1_pack_signs(const void* dense, int32_t dense_dtype, int64_t N, int64_t K, uint32_t* packed, void* scales,
+                        int32_t meta_dtype, uint32_t* inexact, void* stream) {
+  if (dense_dtype != Q1_BF16 && dense_dtype != Q1_F16)
+    return fail(Q1_ERR_INVALID_ARG, "dense dtype must be Q1_BF16 or Q1_F16");
+  if (meta_dtype != Q1_BF16 && meta_dtype != Q1_F16)
+    return fail(Q1_ERR_INVALID_ARG, "metadata dtype must be Q1_BF16 or Q1_F16");
+  if (N <= 0) return fail(Q1_ERR_INVALID_ARG, "N must be positive (got %lld)", (long long)N);
+  if (K <= 0 || K % 128 != 0) return fail(Q1_ERR_INVALID_ARG, "K must be a positive multiple of 128 (got %lld)", (long long)K);
+  if (K > (int64_t)1 << 30 || N > ((int64_t)1 << 40) / K) return fail(Q1_ERR_UNSUPPORTED, "matrix too large");
+  if (dense == nullptr || packed == nullptr || scales == nullptr || inexact == nullptr)
+    return fail(Q1_ERR_INVALID_ARG, "dense, packed, scales and inexact must not be NULL");
+  if (!aligned(dense, 16)) return fail(Q1_ERR_INVALID_ARG, "dense must be 16-byte aligned");
+  if (!aligned(packed, 4) || !aligned(scales, 2) || !aligned(inexact, 4))
+    return fail(Q1_ERR_INVALID_ARG, "packed/inexact must be 4-byte and scales 2-byte aligned");
+  const q1_status st = check_current_device();
+  if (st != Q1_OK) return st;
+  return hip_status(q1::launch_pack(static_cast<const uint16_t*>(dense), dense_dtype == Q1_BF16, N, K, packed,
+                                    static_cast<uint16_t*>(scales), meta_dtype == Q1_BF16, inexact,
+                                    static_cast<hipStream_t>(stream)),
+                    "pack launch");
+}
+
 size_t q1_ffn_workspace_bytes(int64_t M, const q1_weight* gate, const q1_weight* up, const q1_weight* down) {
   if (check_weight(gate, "gate") != Q1_OK || check_weight(up, "up") != Q1_OK || check_weight(down, "down") != Q1_OK)
     return 0;

@@ -171,6 +171,17 @@ hipError_t launch_wide(const WidePlan& plan, const uint16_t* x, int64_t x_ld, co
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* B, int64_t M, int64_t N, int64_t K, void* y,
                             int32_t y_dtype, hipStream_t stream);
 
+// Symmetric-bias check of one affine tensor's metadata (ngroups = N*K/128):
+// *count = groups whose stored bias cannot be replaced by -scale/2 (the
+// counter is cleared by the launch sequence itself).
+hipError_t launch_symcheck(const uint16_t* scales, const uint16_t* biases, int64_t ngroups, bool meta_bf16,
+                           uint32_t* count, hipStream_t stream);
+
+// Sign packer: dense [N, K] (bf16 or fp16) -> packed [N, K/32], scales
+// [N, K/128] (symmetric); *count = groups that do not round-trip exactly.
+hipError_t launch_pack(const uint16_t* dense, bool dense_bf16, int64_t N, int64_t K, uint32_t* packed,
+                       uint16_t* scales, bool meta_bf16, uint32_t* count, hipStream_t stream);
+
 // h[i] = bf16(SiLU(g[i]) * u[i]) for fp32 g, u (n elements).
 hipError_t launch_silu_mul(const float* g, const float* u, uint16_t* h, int64_t n, hipStream_t stream);
 

@@ -40,7 +40,8 @@ _lib = None
 _lib_lock = threading.Lock()
 
 EXPORTS = ["q1_qmm", "q1_qmm_workspace_bytes", "q1_dequantize", "q1_embed_rows", "q1_ffn", "q1_ffn_workspace_bytes",
-           "q1_set_max_packed_rows", "q1_device_supported", "q1_last_error", "q1_version"]
+           "q1_check_symmetric", "q1_pack_signs", "q1_set_max_packed_rows", "q1_device_supported", "q1_last_error",
+           "q1_version"]
 
 
 def load_library(path: str = LIB_PATH):
@@ -62,6 +63,8 @@ def load_library(path: str = LIB_PATH):
             "q1_embed_rows": (i32, [vp, i32, i64, W, vp, i32, vp]),
             "q1_ffn": (i32, [vp, i64, W, W, W, vp, vp, sz, vp]),
             "q1_ffn_workspace_bytes": (sz, [i64, W, W, W]),
+            "q1_check_symmetric": (i32, [W, vp, vp]),
+            "q1_pack_signs": (i32, [vp, i32, i64, i64, vp, vp, i32, vp, vp]),
             "q1_set_max_packed_rows": (ctypes.c_int, [ctypes.c_int]),
             "q1_device_supported": (i32, [ctypes.c_int]),
             "q1_last_error": (ctypes.c_char_p, []),
@@ -263,6 +266,39 @@ def q1_ffn(x: torch.Tensor, gate: PackedQ1, up: PackedQ1, down: PackedQ1, y: Opt
         h = ws[off:off + M * gate.N * 2].view(torch.bfloat16).view(*lead, gate.N).clone()
         return y, h
     return y
+
+
+def q1_check_symmetric(w: PackedQ1, count: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Device int32 [1]: groups of the affine tensor ``w`` whose bias cannot be
+    replaced by -scale/2 (0 means the tensor can drop its biases)."""
+    if w.biases is None:
+        raise ValueError("w is already symmetric")
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=w.scales.device)
+    _check_tensor(count, "count")
+    d = w.desc()
+    _check(load_library().q1_check_symmetric(ctypes.byref(d), ctypes.c_void_p(count.data_ptr()),
+                                             _stream(count.device)))
+    return count
+
+
+def q1_pack_signs(dense: torch.Tensor, meta_dtype: torch.dtype = torch.float16):
+    """Pack dense [N, K] bf16/fp16 weights into a symmetric ``PackedQ1``
+    (scale = 2 max|w| per group of 128, bit = w > 0).  Returns (weight,
+    inexact) with ``inexact`` a device int32 [1]: groups that do not
+    round-trip bit for bit through ``q1_dequantize``."""
+    _check_tensor(dense, "dense")
+    if dense.dim() != 2:
+        raise ValueError("dense must be [N, K]")
+    N, K = dense.shape
+    packed = torch.empty(N, K // 32, dtype=torch.int32, device=dense.device)
+    scales = torch.empty(N, K // 128, dtype=meta_dtype, device=dense.device)
+    inexact = torch.empty(1, dtype=torch.int32, device=dense.device)
+    _check(load_library().q1_pack_signs(ctypes.c_void_p(dense.data_ptr()), _TORCH_TO_Q1.get(dense.dtype, -1), N, K,
+                                        ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                                        _TORCH_TO_Q1.get(meta_dtype, -1), ctypes.c_void_p(inexact.data_ptr()),
+                                        _stream(dense.device)))
+    return PackedQ1(packed, scales, None, int(N), int(K)), inexact
 
 
 def q1_set_max_packed_rows(rows: int) -> int:

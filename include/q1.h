@@ -74,8 +74,13 @@ typedef struct q1_weight {
  *   y        [M, N] in y_dtype (Q1_F32, Q1_BF16 or Q1_F16)
  *   M <= max packed rows (default 8): packed narrow-M kernel, fp32
  *     accumulation, one rounding to y_dtype.
- *   M  > max packed rows: the matrix is dequantised to bf16 in the workspace,
- *     then a bf16 MFMA GEMM with fp32 accumulation runs.
+ *   M  > max packed rows: the wide matrix-core path -- the activations are
+ *     converted once into an fp8 operand image in the workspace, then the
+ *     product runs on the matrix cores straight from the packed weights
+ *     (fp32 accumulation).  With the environment variable
+ *     Q1_WIDE_KERNEL=dequant (read on every call, and by the workspace query)
+ *     the matrix is instead dequantised to bf16 in the workspace and a bf16
+ *     MFMA GEMM runs (Higgs PR #212, "Limitations": the dense fallback).
  *   workspace  device memory of at least q1_qmm_workspace_bytes(M, w) bytes,
  *     256-byte aligned (may be NULL when that query returns 0).  Its first
  *     Q1_WS_RESERVED_BYTES must be zero (see above).  Calls that share one
@@ -119,13 +124,54 @@ q1_status q1_embed_rows(const void* ids, int32_t ids_are_int64, int64_t T, const
  *   M <= max packed rows: gate+up in one packed launch with the SiLU*mul
  *   epilogue (when gate and up share metadata dtype and symmetry; otherwise
  *   two packed launches and an element-wise kernel), then the packed down
- *   projection.  M > max packed rows: dequantise + MFMA GEMM per projection.
+ *   projection.  M > max packed rows: the wide path of q1_qmm per projection
+ *   (gate and up share one activation image when they are the same kind),
+ *   then SiLU*mul, then the down projection.
  *   workspace  q1_ffn_workspace_bytes(...) bytes; same rules as for q1_qmm.
  */
 q1_status q1_ffn(const void* x, int64_t M, const q1_weight* gate, const q1_weight* up, const q1_weight* down,
                  void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 size_t q1_ffn_workspace_bytes(int64_t M, const q1_weight* gate, const q1_weight* up, const q1_weight* down);
+
+/*
+ * q1_check_symmetric -- validation of symmetric metadata stored with an
+ * explicit bias (Higgs PR #212, "What": validate symmetric Q1 metadata and
+ * derive bias = -scale/2; "Walkthrough": loaders compact exact symmetric
+ * biases).
+ *   w      an affine tensor (symmetric = 0, biases non-NULL); only its scales
+ *          and biases are read.
+ *   count  device uint32, written (not accumulated) by the call: the number
+ *          of groups where scale or bias is not finite, or where either code
+ *          dequantises to different fp32 bits with the stored bias than with
+ *          the derived -scale/2 (for a nonzero scale: bias != -scale/2; a zero
+ *          scale accepts either zero bias).
+ *   When *count == 0 the same scales with biases = NULL, symmetric = 1 give
+ *   bit-identical results in every call, without the bias bytes.
+ */
+q1_status q1_check_symmetric(const q1_weight* w, uint32_t* count, void* stream);
+
+/*
+ * q1_pack_signs -- dense weights to a symmetric packed Q1 tensor (Cactus PR
+ * #775, commit notes: groups that hold exactly {-s, +s} repack to sign bits
+ * with zero error and round-trip bit-exactly, linear LSB layout; rMLX issue
+ * #207, "The good news -- packing is standard": bit0 -> -s_g, bit1 -> +s_g).
+ *   dense      [N, K] in dense_dtype (Q1_BF16 or Q1_F16), 16-byte aligned
+ *   packed     out: uint32 [N, K/32]
+ *   scales     out: [N, K/128] in meta_dtype (Q1_BF16 or Q1_F16)
+ *   inexact    device uint32, written by the call: groups that do not
+ *              round-trip (see below)
+ *   Per group of 128 weights: scale = round(2 * max|w|) in meta_dtype, bit =
+ *   (w > 0).  A group is exact when q1_dequantize of the result (to
+ *   dense_dtype) gives back every weight bit for bit -- true for any group
+ *   whose weights are all +v or -v with 2v representable in meta_dtype (and
+ *   v = scale/2 representable in dense_dtype); a group holding a NaN is
+ *   inexact.  Inexact groups are still written (signs and max-magnitude
+ *   scale: a lossy 1-bit code); the count tells the caller whether the
+ *   packing lost anything.
+ */
+q1_status q1_pack_signs(const void* dense, int32_t dense_dtype, int64_t N, int64_t K, uint32_t* packed, void* scales,
+                        int32_t meta_dtype, uint32_t* inexact, void* stream);
 
 /* Largest M served by the packed kernel (1..8, default 8, initial value from
  * the environment variable Q1_QMM_MAX_ROWS).  Returns the previous value, or
