@@ -15,8 +15,10 @@ gap between kernels), and its HBM traffic from the committed rocprofv3 counter
 summary when that summary was taken from the current kernel sources.
 
 The same run also measures, once each, the other rows of the path (tied LM head
-M=1, down projection, embedding gather, dequantisation, the wide M=512 fallback
-and the fused FFN) and times the CPU oracle on a bounded sample of the headline
+M=1, down projection, embedding gather, dequantisation, the wide M=512 product,
+the fused FFN, the sign packer and the symmetric-bias check), a read ceiling
+(one launch that only reads the same number of bytes, for the headline and the
+tied-head sizes), and times the CPU oracle on a bounded sample of the headline
 workload.  Prints one JSON line.
 """
 import argparse
@@ -196,9 +198,22 @@ def main():
         us = run_batch([(lambda W=W, M=M: Q.q1_qmm(x2[:M], W, y=ys[M - 1], workspace=ws2[M])) for W in W2], 3)
         per_m[str(M)] = bw(bytes2, us)
     dom_us = float(np.mean([per_m[str(M)]["us"] for M in DOMINANT_MS]))
+
+    # Read ceiling: one launch that only reads the same number of bytes with
+    # 16-byte loads (consecutive launches read consecutive slices of 1 GiB, so
+    # from HBM).  What a single launch of that size can reach on this part.
+    big = torch.empty(ROTATE_BYTES + (256 << 20), dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def read_ceiling(nbytes):
+        nb = nbytes // 16 * 16
+        n = max(2, ROTATE_BYTES // nb)
+        return bw(nb, run_batch([(lambda i=i: Q.q1_stream_read(big[i * nb:(i + 1) * nb], sink)) for i in range(n)], 3))
+
+    ceiling2 = read_ceiling(bytes2)
     achieved = bytes2 / (dom_us * 1e-6) / 1e9
     traffic = read_traffic()
-    detail = {"ffn_up_5120x17408_sym_f16_per_M": per_m,
+    detail = {"ffn_up_5120x17408_sym_f16_per_M": per_m, "read_ceiling_12533760_bytes": ceiling2,
               "kernels": {"M=1": "q1_gemv_kernel (nibble tables)", "M=2..8": "q1_mma_kernel (fp8 x fp4 MFMA)"}}
 
     if args.copy_calib:
@@ -219,6 +234,7 @@ def main():
         ws4 = ws_for(1, W4[0])
         detail["lm_head_5120x152064_M1"] = bw(w4.metric_bytes, run_batch(
             [(lambda W=W: Q.q1_qmm(x4, W, y=y4, workspace=ws4)) for W in W4], 3))
+        detail["read_ceiling_109486080_bytes"] = read_ceiling(w4.metric_bytes)
         # embedding gather of 4096 ids -> bf16 rows (read packed rows + scales, write bf16)
         ids = torch.from_numpy(wl4.ids).cuda()
         emb = torch.empty(4096, w4.K, dtype=torch.bfloat16, device="cuda")
@@ -246,7 +262,16 @@ def main():
         deq = torch.empty(g5.N, g5.K, dtype=torch.bfloat16, device="cuda")
         deq_bytes = g5.metric_bytes + g5.N * g5.K * 2
         detail["dequant_17408x5120_to_bf16"] = bw(deq_bytes, run_batch([lambda: Q.q1_dequantize(G5, out=deq)], 10))
+        # sign packer on the same shape: read the bf16 matrix, write words and scales
+        pk_bytes = g5.N * g5.K * 2 + g5.metric_bytes
+        detail["pack_signs_17408x5120_bf16_to_q1"] = bw(pk_bytes, run_batch(
+            [lambda: Q.q1_pack_signs(deq, torch.float16)], 10))
         del deq
+        # symmetric check of the down projection's affine metadata (scales + biases read)
+        W3c = Q.PackedQ1.from_host(w3)
+        sc_bytes = 2 * w3.N * (w3.K // 128) * 2
+        detail["check_symmetric_5120x17408_bf16"] = bw(sc_bytes, run_batch([lambda: Q.q1_check_symmetric(W3c)], 20))
+        del W3c
         y5 = torch.empty(512, g5.N, dtype=torch.bfloat16, device="cuda")
         flops = 2.0 * 512 * g5.N * g5.K
         ws5 = ws_for(512, G5)
@@ -314,7 +339,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": DOMINANT, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "avg_launch_us": round(dom_us, 2), "launches": "M=2..8", "bytes_per_launch": bytes2},
+                     "avg_launch_us": round(dom_us, 2), "launches": "M=2..8", "bytes_per_launch": bytes2,
+                     "read_ceiling_GB/s": ceiling2["GB/s"]},
         "cpu_baseline": cpu,
         "detail": detail,
     }

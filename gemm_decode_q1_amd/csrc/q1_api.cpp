@@ -424,6 +424,16 @@ q1_status q1_pack_signs(const void* dense, int32_t dense_dtype, int64_t N, int64
                     "pack launch");
 }
 
+q1_status q1_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream) {
+  if (data == nullptr || sink == nullptr) return fail(Q1_ERR_INVALID_ARG, "data and sink must not be NULL");
+  if (!aligned(data, 16) || bytes % 16 != 0) return fail(Q1_ERR_INVALID_ARG, "data must be 16-byte aligned, bytes a multiple of 16");
+  if (bytes >= ((size_t)1 << 31)) return fail(Q1_ERR_UNSUPPORTED, "bytes must be below 2^31");
+  const q1_status st = check_current_device();
+  if (st != Q1_OK) return st;
+  if (bytes == 0) return ok();
+  return hip_status(q1::launch_read(data, bytes, sink, static_cast<hipStream_t>(stream)), "read launch");
+}
+
 size_t q1_ffn_workspace_bytes(int64_t M, const q1_weight* gate, const q1_weight* up, const q1_weight* down) {
   if (check_weight(gate, "gate") != Q1_OK || check_weight(up, "up") != Q1_OK || check_weight(down, "down") != Q1_OK)
     return 0;

@@ -182,6 +182,9 @@ hipError_t launch_symcheck(const uint16_t* scales, const uint16_t* biases, int64
 hipError_t launch_pack(const uint16_t* dense, bool dense_bf16, int64_t N, int64_t K, uint32_t* packed,
                        uint16_t* scales, bool meta_bf16, uint32_t* count, hipStream_t stream);
 
+// One read pass over `bytes` bytes (16-byte loads), for the read ceiling.
+hipError_t launch_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 // h[i] = bf16(SiLU(g[i]) * u[i]) for fp32 g, u (n elements).
 hipError_t launch_silu_mul(const float* g, const float* u, uint16_t* h, int64_t n, hipStream_t stream);
 

@@ -11,8 +11,8 @@
 //                     format of rMLX issue #207 (bit0 -> -s_g, bit1 -> +s_g,
 //                     stored scale 2 s_g, symmetric).
 //
-// Both are HBM-bound streams; both count through one device counter that a
-// one-thread kernel clears first (a kernel, not a memset, so the calls can be
+// Both are HBM-bound streams; both count through one device counter (one
+// atomic per workgroup) that a one-thread kernel clears first (a kernel, not a memset, so the calls can be
 // captured in a graph).
 #include <hip/hip_runtime.h>
 
@@ -41,11 +41,22 @@ int meta_device_cus() {
 
 __device__ __forceinline__ bool finite_f32(float v) { return (__float_as_uint(v) & 0x7f800000u) != 0x7f800000u; }
 
-// Add the wave's count of lanes with `flag` set to *count (one atomic per
-// wave).  Every lane of the wave must call it.
-__device__ __forceinline__ void wave_count(bool flag, uint32_t* count) {
-  const uint64_t m = __ballot(flag);
-  if ((threadIdx.x & 63) == 0 && m != 0) atomicAdd(count, (uint32_t)__popcll(m));
+constexpr int kMetaThreads = 1024;
+
+// Add the workgroup's per-thread counts to *count: a wave sum, a sum of the
+// waves in LDS, then one atomic per workgroup (only when nonzero).  Every
+// thread of the workgroup must call it.  Atomics on the one counter serialise,
+// so the launches keep to two workgroups per CU.
+__device__ __forceinline__ void block_count(uint32_t v, uint32_t* count) {
+  __shared__ uint32_t part[kMetaThreads / 64];
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t sum = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) sum += part[w];
+    if (sum != 0) atomicAdd(count, sum);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -55,7 +66,7 @@ __device__ __forceinline__ void wave_count(bool flag, uint32_t* count) {
 // nonzero scale that is b == -s/2; a zero scale accepts either zero.)
 // ---------------------------------------------------------------------------
 template <bool MBF16>
-__global__ __launch_bounds__(256) void q1_symcheck_kernel(const uint16_t* __restrict__ scales,
+__global__ __launch_bounds__(kMetaThreads) void q1_symcheck_kernel(const uint16_t* __restrict__ scales,
                                                           const uint16_t* __restrict__ biases, int64_t ngroups,
                                                           uint32_t* __restrict__ count) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -70,9 +81,7 @@ __global__ __launch_bounds__(256) void q1_symcheck_kernel(const uint16_t* __rest
                       __float_as_uint(__builtin_fmaf(s, 1.0f, b)) == __float_as_uint(__builtin_fmaf(s, 1.0f, d));
     bad += same ? 0u : 1u;
   }
-  // wave sum, then one atomic per wave
-  for (int off = 32; off > 0; off >>= 1) bad += __shfl_xor(bad, off);
-  if ((threadIdx.x & 63) == 0 && bad != 0) atomicAdd(count, bad);
+  block_count(bad, count);
 }
 
 // ---------------------------------------------------------------------------
@@ -108,15 +117,16 @@ __device__ __forceinline__ uint32_t quad_and(uint32_t v) {
 }
 
 template <bool DBF16, bool MBF16>
-__global__ __launch_bounds__(256) void q1_pack_kernel(const uint16_t* __restrict__ dense, int64_t nwords,
+__global__ __launch_bounds__(kMetaThreads) void q1_pack_kernel(const uint16_t* __restrict__ dense, int64_t nwords,
                                                       uint32_t* __restrict__ packed, uint16_t* __restrict__ scales,
                                                       uint32_t* __restrict__ count) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;  // a multiple of 64
   // Every lane runs the same number of iterations (indices past the end are
-  // clamped and their results dropped), so the quad exchanges and the wave
-  // ballot always see whole, active waves.
+  // clamped and their results dropped), so the quad exchanges always see
+  // whole, active quads.
   const int64_t base0 = (int64_t)blockIdx.x * blockDim.x;
   const int64_t iters = nwords > base0 ? (nwords - base0 + stride - 1) / stride : 0;
+  uint32_t bad = 0;
   for (int64_t it = 0; it < iters; ++it) {
     const int64_t t = base0 + it * stride + threadIdx.x;
     const bool live = t < nwords;  // nwords % 4 == 0: quads are live or dead together
@@ -158,24 +168,51 @@ __global__ __launch_bounds__(256) void q1_pack_kernel(const uint16_t* __restrict
       packed[t] = word;
       if ((t & 3) == 0) scales[t >> 2] = (uint16_t)sbits;
     }
-    wave_count(live && (t & 3) == 0 && exact == 0u, count);
+    bad += (live && (t & 3) == 0 && exact == 0u) ? 1u : 0u;
   }
+  block_count(bad, count);
+}
+
+// ---------------------------------------------------------------------------
+// Read ceiling (measurement aid): one pass over `bytes` bytes with 16-byte
+// non-temporal buffer loads, the access the packed kernels make, and nothing
+// else.  The XOR of the data is stored only if it equals a sentinel, which
+// keeps the loads alive without a store per workgroup.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(1024) void q1_read_kernel(const void* data, uint32_t bytes, uint32_t* sink) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(data), (short)0, (int)bytes, (int)0x00020000);
+  const uint32_t nvec = bytes >> 4;
+  uint32_t acc = 0u;
+  for (uint32_t i = blockIdx.x * 1024u + threadIdx.x; i < nvec; i += gridDim.x * 1024u) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, i * 16u, 0, 2);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if (acc == 0x9E3779B9u) *sink = acc;
 }
 
 }  // namespace
 
+hipError_t launch_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  const int64_t blocks = (int64_t)meta_device_cus() * 2;  // two 1024-thread workgroups per CU
+  hipLaunchKernelGGL(q1_read_kernel, dim3((unsigned)blocks), dim3(1024), 0, stream, data, (uint32_t)bytes, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_symcheck(const uint16_t* scales, const uint16_t* biases, int64_t ngroups, bool meta_bf16,
                            uint32_t* count, hipStream_t stream) {
   hipLaunchKernelGGL(q1_clear_u32, dim3(1), dim3(1), 0, stream, count);
-  int64_t blocks = (ngroups + 255) / 256;
-  const int64_t cap = (int64_t)meta_device_cus() * 8;
+  int64_t blocks = (ngroups + kMetaThreads - 1) / kMetaThreads;
+  const int64_t cap = (int64_t)meta_device_cus() / 2;  // metadata is small: few workgroups, few atomics
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   if (meta_bf16)
-    hipLaunchKernelGGL((q1_symcheck_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, stream, scales, biases,
+    hipLaunchKernelGGL((q1_symcheck_kernel<true>), dim3((unsigned)blocks), dim3(kMetaThreads), 0, stream, scales, biases,
                        ngroups, count);
   else
-    hipLaunchKernelGGL((q1_symcheck_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, stream, scales, biases,
+    hipLaunchKernelGGL((q1_symcheck_kernel<false>), dim3((unsigned)blocks), dim3(kMetaThreads), 0, stream, scales, biases,
                        ngroups, count);
   return hipGetLastError();
 }
@@ -184,12 +221,12 @@ hipError_t launch_pack(const uint16_t* dense, bool dense_bf16, int64_t N, int64_
                        uint16_t* scales, bool meta_bf16, uint32_t* count, hipStream_t stream) {
   hipLaunchKernelGGL(q1_clear_u32, dim3(1), dim3(1), 0, stream, count);
   const int64_t nwords = N * (K / 32);
-  int64_t blocks = (nwords + 255) / 256;
-  const int64_t cap = (int64_t)meta_device_cus() * 8;
+  int64_t blocks = (nwords + kMetaThreads - 1) / kMetaThreads;
+  const int64_t cap = (int64_t)meta_device_cus() * 2;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
 #define Q1_PK(D, MB)                                                                                       \
-  hipLaunchKernelGGL((q1_pack_kernel<D, MB>), dim3((unsigned)blocks), dim3(256), 0, stream, dense, nwords, \
+  hipLaunchKernelGGL((q1_pack_kernel<D, MB>), dim3((unsigned)blocks), dim3(kMetaThreads), 0, stream, dense, nwords, \
                      packed, scales, count)
   if (dense_bf16) {
     if (meta_bf16) Q1_PK(true, true);

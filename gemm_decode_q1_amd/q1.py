@@ -40,7 +40,7 @@ _lib = None
 _lib_lock = threading.Lock()
 
 EXPORTS = ["q1_qmm", "q1_qmm_workspace_bytes", "q1_dequantize", "q1_embed_rows", "q1_ffn", "q1_ffn_workspace_bytes",
-           "q1_check_symmetric", "q1_pack_signs", "q1_set_max_packed_rows", "q1_device_supported", "q1_last_error",
+           "q1_check_symmetric", "q1_pack_signs", "q1_stream_read", "q1_set_max_packed_rows", "q1_device_supported", "q1_last_error",
            "q1_version"]
 
 
@@ -65,6 +65,7 @@ def load_library(path: str = LIB_PATH):
             "q1_ffn_workspace_bytes": (sz, [i64, W, W, W]),
             "q1_check_symmetric": (i32, [W, vp, vp]),
             "q1_pack_signs": (i32, [vp, i32, i64, i64, vp, vp, i32, vp, vp]),
+            "q1_stream_read": (i32, [vp, sz, vp, vp]),
             "q1_set_max_packed_rows": (ctypes.c_int, [ctypes.c_int]),
             "q1_device_supported": (i32, [ctypes.c_int]),
             "q1_last_error": (ctypes.c_char_p, []),
@@ -299,6 +300,15 @@ def q1_pack_signs(dense: torch.Tensor, meta_dtype: torch.dtype = torch.float16):
                                         _TORCH_TO_Q1.get(meta_dtype, -1), ctypes.c_void_p(inexact.data_ptr()),
                                         _stream(dense.device)))
     return PackedQ1(packed, scales, None, int(N), int(K)), inexact
+
+
+def q1_stream_read(data: torch.Tensor, sink: torch.Tensor) -> None:
+    """One read pass over ``data`` (measurement aid: the single-launch read
+    ceiling for that many bytes).  ``sink`` is a device int32 [1]."""
+    _check_tensor(data, "data")
+    _check_tensor(sink, "sink")
+    _check(load_library().q1_stream_read(ctypes.c_void_p(data.data_ptr()), data.numel() * data.element_size(),
+                                         ctypes.c_void_p(sink.data_ptr()), _stream(data.device)))
 
 
 def q1_set_max_packed_rows(rows: int) -> int:

@@ -173,6 +173,17 @@ q1_status q1_check_symmetric(const q1_weight* w, uint32_t* count, void* stream);
 q1_status q1_pack_signs(const void* dense, int32_t dense_dtype, int64_t N, int64_t K, uint32_t* packed, void* scales,
                         int32_t meta_dtype, uint32_t* inexact, void* stream);
 
+/*
+ * q1_stream_read -- measurement aid, not a step of the decode path: one pass
+ * that reads `bytes` bytes at `data` with 16-byte non-temporal loads (the
+ * access of the packed kernels) and computes nothing else.  Its duration is
+ * the ceiling a single launch reading that many bytes can reach, the context
+ * for the HBM rooflines of the other calls.
+ *   data   device memory, 16-byte aligned; bytes a multiple of 16, < 2^31
+ *   sink   device uint32, written only if the data XOR to a fixed sentinel
+ */
+q1_status q1_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream);
+
 /* Largest M served by the packed kernel (1..8, default 8, initial value from
  * the environment variable Q1_QMM_MAX_ROWS).  Returns the previous value, or
  * -1 (value unchanged) when rows is outside 1..8.  (Higgs PR #212,
