@@ -1,9 +1,11 @@
 // C ABI of the packed Q1 library: argument validation, dispatch between the
-// packed narrow-M kernel and the dense fallback, workspace layout.
+// packed narrow-M kernels and the wide path, workspace layout.
 //
 // Dispatch rule (Higgs PR #212, "What" and "Limitations"): Q1 matmuls of up
-// to 8 flattened rows stay packed; wider ones dequantise to the activation
-// dtype (bf16) and run a dense GEMM.  The row threshold is an override.
+// to 8 flattened rows stay packed; wider ones take the wide path -- here the
+// matrix cores straight from the packed words, or (Q1_WIDE_KERNEL=dequant) the
+// pages' dense fallback, dequantisation to bf16 and a dense GEMM.  The row
+// threshold is an override.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
