@@ -292,12 +292,17 @@ bool plan_gemv(int M, int64_t N, int64_t K, bool pair, bool affine, GemvPlan* p,
   }
   p->lds_bytes = (size_t)gemv_lds_bytes(M);
   p->threads = gemv_threads(M);
-  // Workgroups: as many as are resident at once (one or two per CU, by LDS),
-  // the units split evenly over them (an even count each, so gate/up pairs
-  // never straddle two workgroups).  A second round of workgroups on a few
-  // CUs would double those CUs' work, so the count never exceeds the slots.
-  const int per_cu = (int)((160 * 1024) / p->lds_bytes) >= 2 ? 2 : 1;
-  const int64_t slots = (int64_t)device_cus() * per_cu;
+  // Workgroups: as many as are resident at once, the units split evenly over
+  // them (an even count each, so gate/up pairs never straddle two
+  // workgroups).  A second round of workgroups on a few CUs would double
+  // those CUs' work, so the count never exceeds the resident slots.  A
+  // second workgroup per CU (when the tables leave room for it) builds the
+  // same tables again and launches twice the waves: it pays only when each CU
+  // has many rows to stream (measured: one per CU at 68 rows per CU, FFN
+  // up/gate; two at 594, the tied head).
+  const int cus = device_cus();
+  const bool two = (int)((160 * 1024) / p->lds_bytes) >= 2 && p->units >= (int64_t)256 * cus;
+  const int64_t slots = (int64_t)cus * (two ? 2 : 1);
   const int64_t wx = slots / p->KS > 0 ? slots / p->KS : 1;
   int64_t upw = (p->units + wx - 1) / wx;
   upw += upw & 1;
