@@ -161,3 +161,37 @@ def test_errors_are_reported():
     with pytest.raises(Q.Q1Error):
         Q.q1_pack_signs(bad)
     assert "multiple of 128" in Q.q1_last_error()
+
+
+def test_meta_calls_replay_in_a_graph():
+    """Both calls captured once in a HIP graph and replayed several times, with
+    eager changes to their inputs between replays: every replay clears its
+    counter and counts afresh (the counters are cleared by a kernel, not a
+    memset node)."""
+    rng = np.random.Generator(np.random.PCG64(300))
+    N, K = 64, 1024
+    w = S.draw_weight(rng, N, K, "bf16", True)
+    half = O.round_to((np.float32(-0.5) * O.meta_to_f32(w.scales, "bf16")).astype(np.float32), "bf16")
+    P = torch.from_numpy(w.packed.view(np.int32)).cuda()
+    sc, bi = dev16(w.scales, "bf16"), dev16(half, "bf16")
+    W = Q.PackedQ1(P, sc, bi, N, K)
+    dense = Q.q1_dequantize(Q.PackedQ1(P, sc, None, N, K), torch.bfloat16)
+    count = torch.empty(1, dtype=torch.int32, device="cuda")
+    Q.q1_check_symmetric(W, count)
+    Wp, bad = Q.q1_pack_signs(dense, torch.bfloat16)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        Q.q1_check_symmetric(W, count)
+        Wp, bad = Q.q1_pack_signs(dense, torch.bfloat16)
+    bias_bits, dense_bits = bi.view(torch.int16), dense.view(torch.int16)
+    for step in range(4):
+        if step > 0:  # eager changes between replays: one more bad bias, one more inexact group
+            bias_bits[step, 0] ^= 1
+            dense_bits[step, 3] ^= 1
+        g.replay()
+        torch.cuda.synchronize()
+        exp_check = O.symmetric_mismatches(w.scales, host16(bi), "bf16")
+        _, _, exp_bad = O.pack_signs(host16(dense), "bf16", "bf16")
+        assert exp_check == step and exp_bad == step
+        assert int(count.item()) == exp_check and int(bad.item()) == exp_bad
