@@ -195,3 +195,21 @@ def test_meta_calls_replay_in_a_graph():
         _, _, exp_bad = O.pack_signs(host16(dense), "bf16", "bf16")
         assert exp_check == step and exp_bad == step
         assert int(count.item()) == exp_check and int(bad.item()) == exp_bad
+
+
+def test_stream_read_reads_its_input():
+    """The read-ceiling aid really reads the data: one 16-byte vector whose
+    words XOR to the sentinel makes the kernel store it; any other data leaves
+    the sink alone.  Bad sizes and alignment are rejected."""
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    data = torch.tensor([0x9E3779B9 - (1 << 32), 0, 0, 0], dtype=torch.int64).to(torch.int32).cuda()
+    Q.q1_stream_read(torch.tensor([1, 0, 0, 0], dtype=torch.int32, device="cuda"), sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    Q.q1_stream_read(data, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) & 0xFFFFFFFF == 0x9E3779B9
+    with pytest.raises(Q.Q1Error):
+        Q.q1_stream_read(torch.zeros(3, dtype=torch.int32, device="cuda"), sink)  # 12 bytes
+    with pytest.raises(Q.Q1Error):
+        Q.q1_stream_read(torch.zeros(8, dtype=torch.int32, device="cuda")[1:5], sink)  # misaligned
