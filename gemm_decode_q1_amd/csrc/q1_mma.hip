@@ -285,7 +285,11 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   constexpr int RB = MR == 4 ? 8 : MR;  // A rows kept in LDS per half
   using Lay = ALay<RB>;
   constexpr int NMAT = PAIR ? 2 : 1;
-  constexpr int D = PAIR ? 2 : 4;
+  // Ring slots (items in flight + those being computed).  Two: more items in
+  // flight per wave congest the memory pipeline the waves issue into
+  // (measured at K=5120, N=17408: 2 slots 2-5 % faster than 4 at M=2..8;
+  // at K=17408, N=5120 9 % at M=1, 2; 3, 5, 6 slots slower than 4 at M=4).
+  constexpr int D = 2;
   constexpr int NSC = SC128 ? 4 : 8;  // registers of metadata per row and item
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int last_flag;
