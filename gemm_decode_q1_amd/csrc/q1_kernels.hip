@@ -55,7 +55,23 @@ __device__ __forceinline__ uint32_t div_by(uint32_t t, DivMagic dm) {
   return (uint32_t)(((uint64_t)__umulhi(t, dm.m) + t) >> dm.l);
 }
 
-template <int OUT, bool MBF16>
+typedef float f32x4_st __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_st __attribute__((ext_vector_type(4)));
+
+// 16-byte output store.  Gathered rows are written with the non-temporal
+// hint (measured 22 % faster for 4096 rows of K = 5120); a whole dequantised
+// matrix keeps normal stores, since it usually feeds a product right away and
+// (at 178 MB for the FFN shapes) can stay in the last-level cache for it.
+template <bool NT, typename V>
+__device__ __forceinline__ void store16(V* p, V v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
+// GATHER: rows are selected by `ids` (embedding lookup), else rows 0..T-1.
+template <int OUT, bool MBF16, bool GATHER>
 __global__ __launch_bounds__(256) void q1_dequant_kernel(const uint32_t* __restrict__ packed,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint16_t* __restrict__ biases, int symmetric,
@@ -75,7 +91,7 @@ __global__ __launch_bounds__(256) void q1_dequant_kernel(const uint32_t* __restr
       r[u] = div_by(t, per_row_div);
       piece[u] = t - r[u] * per_row;
       row[u] = r[u];
-      if (ids != nullptr && t < total)
+      if (GATHER && t < total)
         row[u] = ids64 ? static_cast<const int64_t*>(ids)[r[u]] : (int64_t) static_cast<const int32_t*>(ids)[r[u]];
     }
     uint32_t word[kDqU], sb[kDqU], bb[kDqU];
@@ -110,9 +126,9 @@ __global__ __launch_bounds__(256) void q1_dequant_kernel(const uint32_t* __restr
         float vals[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) vals[j] = ((bits >> j) & 1u) ? v1 : v0;
-        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + o);
-        dst[0] = make_float4(vals[0], vals[1], vals[2], vals[3]);
-        dst[1] = make_float4(vals[4], vals[5], vals[6], vals[7]);
+        f32x4_st* dst = reinterpret_cast<f32x4_st*>(static_cast<float*>(out) + o);
+        store16<GATHER>(dst, f32x4_st{vals[0], vals[1], vals[2], vals[3]});
+        store16<GATHER>(dst + 1, f32x4_st{vals[4], vals[5], vals[6], vals[7]});
       } else {
         const uint32_t o0 = (OUT == BF16) ? f32_to_bf16_bits(v0) : f32_to_f16_bits(v0);
         const uint32_t o1 = (OUT == BF16) ? f32_to_bf16_bits(v1) : f32_to_f16_bits(v1);
@@ -123,7 +139,7 @@ __global__ __launch_bounds__(256) void q1_dequant_kernel(const uint32_t* __restr
           const uint32_t hi = ((bits >> (2 * j + 1)) & 1u) ? o1 : o0;
           d[j] = lo | (hi << 16);
         }
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o) = make_uint4(d[0], d[1], d[2], d[3]);
+        store16<GATHER>(reinterpret_cast<u32x4_st*>(static_cast<uint16_t*>(out) + o), u32x4_st{d[0], d[1], d[2], d[3]});
       }
     }
   }
@@ -415,9 +431,15 @@ hipError_t launch_dequant(const QMat& w, const void* ids, int ids_int64, int64_t
     const uint16_t* bi = (ids == nullptr && w.biases != nullptr) ? w.biases + r0 * (w.K >> 7) : w.biases;
     const int64_t nrows = ids == nullptr ? tr : w.N;
     void* o = static_cast<char*>(out) + (size_t)r0 * (size_t)w.K * osz;
-#define Q1_DQ(OUT, MB)                                                                                             \
-  hipLaunchKernelGGL((q1_dequant_kernel<OUT, MB>), dim3((unsigned)blocks), dim3(256), 0, stream, pk, sc, bi, sym, \
-                     nrows, w.K, ids_c, ids_int64, total, dm, o)
+#define Q1_DQ(OUT, MB)                                                                                      \
+  do {                                                                                                       \
+    if (ids != nullptr)                                                                                      \
+      hipLaunchKernelGGL((q1_dequant_kernel<OUT, MB, true>), dim3((unsigned)blocks), dim3(256), 0, stream, pk, \
+                         sc, bi, sym, nrows, w.K, ids_c, ids_int64, total, dm, o);                            \
+    else                                                                                                     \
+      hipLaunchKernelGGL((q1_dequant_kernel<OUT, MB, false>), dim3((unsigned)blocks), dim3(256), 0, stream,   \
+                         pk, sc, bi, sym, nrows, w.K, ids_c, ids_int64, total, dm, o);                        \
+  } while (0)
     if (w.meta_bf16) {
       if (out_dtype == F32) Q1_DQ(F32, true);
       else if (out_dtype == F16) Q1_DQ(F16, true);
