@@ -15,6 +15,7 @@
 #include <mutex>
 
 #include "../../include/q1.h"
+#include "../../include/q1_measure.h"
 #include "q1_internal.h"
 
 namespace {
@@ -119,21 +120,18 @@ constexpr size_t kReserved = Q1_WS_RESERVED_BYTES;
 // Packed narrow-M launches: the nibble-table kernel (q1_gemv.inc) for one
 // activation row, the matrix-core kernel (q1_mma.hip) for 2..8 rows, where
 // table lookups grow with the row count.  Q1_PACKED_KERNEL=table|mma forces
-// one of them for every row count.
+// one of them for every row count (read on every call, like
+// Q1_WIDE_KERNEL; the workspace query must see the same setting as the call).
 // 0: default routing, 1: table kernel forced, 2: matrix-core kernel forced
 int packed_kernel_env() {
-  static const int v = [] {
-    const char* e = getenv("Q1_PACKED_KERNEL");
-    if (e && strcmp(e, "table") == 0) return 1;
-    if (e && strcmp(e, "mma") == 0) return 2;
-    return 0;
-  }();
-  return v;
+  const char* e = getenv("Q1_PACKED_KERNEL");
+  if (e && strcmp(e, "table") == 0) return 1;
+  if (e && strcmp(e, "mma") == 0) return 2;
+  return 0;
 }
 
 // More than 8 rows: the wide matrix-core kernel straight from the packed
-// weights; Q1_WIDE_KERNEL=dequant selects the dequantise-to-bf16 + GEMM path.
-// Q1_WIDE_KERNEL=dequant selects the dense fallback (dequantise to bf16, then
+// weights.  Q1_WIDE_KERNEL=dequant selects the dense fallback (dequantise to bf16, then
 // the bf16 GEMM) for M > max rows; read on every call, so a caller can switch
 // between the two wide paths (the workspace query must see the same setting
 // as the call it sizes).

@@ -30,6 +30,9 @@ constexpr int gemv_lds_bytes(int M) { return (gemv_krmax(M) - 1) * gemv_chunk_bl
 // (Q1_WS_RESERVED_BYTES in the public header).
 constexpr int kCounterBytes = 16384;
 
+// Compute units of the current device (cached per device id).
+int device_cus();
+
 struct QMat {
   const uint32_t* packed;
   const uint16_t* scales;
@@ -69,7 +72,6 @@ struct GemvArgs {
   int32_t K, wpr, gpr, chunks;
   int32_t KS, pair;
   int32_t full_chunks;   // chunks with all 32 words inside the row (K / 1024)
-  int32_t fused_splitk;  // 1: finish split-K in the kernel (arrival counters)
   int64_t units, units_per_wg;
   uint32_t packed_bytes;  // N * K / 8      (< 2^31)
   uint32_t meta_bytes;    // N * K / 128 * 2 (< 2^31)

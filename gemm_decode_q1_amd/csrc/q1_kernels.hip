@@ -273,14 +273,20 @@ __global__ __launch_bounds__(256) void q1_splitk_reduce(const float* __restrict_
 // Host launchers
 // ---------------------------------------------------------------------------
 
-static int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
+int device_cus() {
+  // cached per device id; the plans of every kernel size their grids by it
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev < 0 || dev >= 64) {
     int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cus = v;
+    return hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0 ? v : 256;
+  }
+  int cus = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (cus == 0) {
+    int v = 0;
+    cus = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0 ? v : 256;
+    __atomic_store_n(&cache[dev], cus, __ATOMIC_RELAXED);
   }
   return cus;
 }
@@ -334,15 +340,6 @@ bool plan_gemv(int M, int64_t N, int64_t K, bool pair, bool affine, GemvPlan* p,
   return true;
 }
 
-static bool fused_splitk_enabled() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("Q1_SPLITK_FUSED");
-    v = (e && e[0] == '1') ? 1 : 0;
-  }
-  return v == 1;
-}
-
 template <int M>
 static hipError_t launch_reduce_m(const GemvPlan& plan, const GemvArgs& g, hipStream_t stream) {
   const int64_t upb = 512;  // even, so gate/up pairs never straddle blocks
@@ -371,7 +368,6 @@ hipError_t launch_gemv(const GemvPlan& plan, const uint16_t* x, int64_t x_ld, co
   g.KS = plan.KS;
   g.pair = b ? 1 : 0;
   g.full_chunks = (int32_t)(a.K / kChunkK);
-  g.fused_splitk = (plan.KS > 1 && fused_splitk_enabled()) ? 1 : 0;
   g.units = plan.units;
   g.units_per_wg = plan.units_per_wg;
   g.packed_bytes = (uint32_t)(a.N * (a.K / 8));
@@ -395,7 +391,7 @@ hipError_t launch_gemv(const GemvPlan& plan, const uint16_t* x, int64_t x_ld, co
     case 8: e = launch_gemv_m<8>(plan, g, affine, mbf16, stream); break;
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess || plan.KS == 1 || g.fused_splitk) return e;
+  if (e != hipSuccess || plan.KS == 1) return e;
   switch (plan.M) {
     case 1: return launch_reduce_m<1>(plan, g, stream);
     case 2: return launch_reduce_m<2>(plan, g, stream);

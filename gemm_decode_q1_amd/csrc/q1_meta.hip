@@ -26,19 +26,6 @@ namespace {
 
 __global__ void q1_clear_u32(uint32_t* p) { *p = 0u; }
 
-int meta_device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-    else
-      cus = 256;
-  }
-  return cus;
-}
-
 __device__ __forceinline__ bool finite_f32(float v) { return (__float_as_uint(v) & 0x7f800000u) != 0x7f800000u; }
 
 constexpr int kMetaThreads = 1024;
@@ -196,7 +183,7 @@ __global__ __launch_bounds__(1024) void q1_read_kernel(const void* data, uint32_
 }  // namespace
 
 hipError_t launch_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream) {
-  const int64_t blocks = (int64_t)meta_device_cus() * 2;  // two 1024-thread workgroups per CU
+  const int64_t blocks = (int64_t)device_cus() * 2;  // two 1024-thread workgroups per CU
   hipLaunchKernelGGL(q1_read_kernel, dim3((unsigned)blocks), dim3(1024), 0, stream, data, (uint32_t)bytes, sink);
   return hipGetLastError();
 }
@@ -205,7 +192,7 @@ hipError_t launch_symcheck(const uint16_t* scales, const uint16_t* biases, int64
                            uint32_t* count, hipStream_t stream) {
   hipLaunchKernelGGL(q1_clear_u32, dim3(1), dim3(1), 0, stream, count);
   int64_t blocks = (ngroups + kMetaThreads - 1) / kMetaThreads;
-  const int64_t cap = (int64_t)meta_device_cus() / 2;  // metadata is small: few workgroups, few atomics
+  const int64_t cap = (int64_t)device_cus() / 2;  // metadata is small: few workgroups, few atomics
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   if (meta_bf16)
@@ -222,7 +209,7 @@ hipError_t launch_pack(const uint16_t* dense, bool dense_bf16, int64_t N, int64_
   hipLaunchKernelGGL(q1_clear_u32, dim3(1), dim3(1), 0, stream, count);
   const int64_t nwords = N * (K / 32);
   int64_t blocks = (nwords + kMetaThreads - 1) / kMetaThreads;
-  const int64_t cap = (int64_t)meta_device_cus() * 2;
+  const int64_t cap = (int64_t)device_cus() * 2;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
 #define Q1_PK(D, MB)                                                                                       \

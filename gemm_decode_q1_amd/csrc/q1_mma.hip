@@ -21,14 +21,28 @@
 //     symmetric: sum w x = s (S - X/2),  affine: sum w x = s S + b X,
 //   with X the group sum of x: for symmetric tensors -X/2 enters as the
 //   MFMA's accumulator input, for affine ones b X is added after it.
-// * A operand: each activation as two fp8 (E4M3) pieces, x = hi + lo/16, with
-//   one power-of-two block scale per 32 weights chosen from the block's
-//   largest |x|.  A bf16 value has 8 significant bits, hi carries the top 4
-//   (rounded) and lo the rest, so the pair is exact for every element within
-//   2^12 of its block's largest magnitude; below that the error is at most
-//   2^-19 of the block maximum.  Rows 0..7 of the 16-row A tile hold hi for the M
-//   activation rows and rows 8..15 hold lo; the two halves of the result are
-//   added at the end.
+// * A operand, symmetric tensors: each activation as two fp8 (E4M3) pieces,
+//   x = hi + lo/16, with one power-of-two block scale per 32 weights chosen
+//   from the block's largest |x|.  A bf16 value has 8 significant bits, hi
+//   carries the top 4 (rounded) and lo the rest, so the pair is exact for
+//   every element within 2^11 of its block's largest magnitude; below that
+//   the error is at most 2^-19 of the block maximum, and since every weight
+//   of a symmetric group has the same magnitude s/2, the product's error
+//   stays below 2^-14 s sum|x| -- an eighth of the tolerance.  Rows 0..7 of
+//   the 16-row A tile hold hi for the M activation rows and rows 8..15 hold
+//   lo; the two halves of the result are added at the end.
+// * Affine tensors: the weights of a group are w1 = fl(s + b) (set bits) and
+//   w0 = b (clear bits), of any relative size, so an error relative to the
+//   block's largest |x| is not relative to sum |w x|.  Two changes make it so:
+//   (1) each activation is split into three E5M2 (bf8) pieces with their own
+//   block scales, exact for every element within 2^25 of its block maximum
+//   (q1_fp8.h); piece p of activation row m is A row 4p + m % 4 of row tile
+//   m / 4 (rows 12..15 hold zeros); (2) per weight row and group the product
+//   runs over the code class d whose weight is larger in magnitude (the B
+//   word is complemented when d = 0), and the group's contribution is
+//     (w_d - w_o) S_d + w_o X,   S_d = sum of x over the codes equal to d,
+//   so the rounding of X and of the fp32 sums is multiplied by the smaller
+//   weight w_o, and S_d's error by 2 |w_d|, both within the tolerance.
 // * One instruction covers 16 weight rows x one group (128 weights): its fp32
 //   result is multiplied by the group scale (and the bias term added) on the
 //   vector ALU.
@@ -102,6 +116,22 @@ struct ALay {
   }
 };
 constexpr int span_bytes(int rb) { return rb == 8 ? 4 * 2064 + 512 : 1024 * rb + 512; }
+
+// LDS image of one span for affine tensors (RT row tiles of 4 activation
+// rows): per row tile an A operand image laid out as ALay<8> (rows 4p + i:
+// piece p of activation row 4 rt + i; rows 12..15 zero), the block scales
+// [rt][64 lanes][4 groups] bytes, and the group sums [g4][rt][16] floats (X of
+// activation row 4 rt + i in entry i for the piece-0 lanes, zero in entries
+// 4..15, so only one quarter of the result adds w_o X).
+template <int RT>
+struct AffLay {
+  static constexpr int kTileA = 4 * 2064;
+  static constexpr int kA = RT * kTileA;
+  static constexpr int kSc = kA;
+  static constexpr int kXs = kA + RT * 256;
+  static constexpr int kSpan = kA + RT * 512;
+};
+constexpr int aff_span_bytes(int rt) { return rt * (4 * 2064 + 512); }
 
 // per-wave LDS scratch of the word transpose: 16 rows x 34 dwords (32 used)
 constexpr int kScrStride = 34;
@@ -211,6 +241,75 @@ __device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int 
   }
 }
 
+// Affine conversion (AffLay<RT>): three E5M2 pieces per activation.  Zeroes
+// A rows 12..15 and their scale bytes (1.0), and the group-sum entries no
+// live piece-0 lane owns; the rows of activation index >= M inside a row
+// tile are left unwritten (the MFMA keeps rows apart, and those results are
+// never read).
+template <int RT>
+__device__ void prep_compute_aff(const MmaArgs& a, int nsp, unsigned char* lds, int tid, const PrepLoads& L) {
+  using Lay = AffLay<RT>;
+  using AL = ALay<8>;
+  // zero rows 12..15: per span and row tile, 8 blocks x 4 quarters x 4 rows
+  for (int idx = tid; idx < nsp * RT * 128; idx += kThreads) {
+    const int c = idx & 127, srt = idx >> 7;
+    const int sp = srt / RT, rt = srt - sp * RT;
+    const int blk = c >> 4, qa = (c >> 2) & 3, r = 12 + (c & 3);
+    *reinterpret_cast<u32x4*>(lds + sp * Lay::kSpan + rt * Lay::kTileA + AL::chunk(blk, qa, r)) = u32x4{0u, 0u, 0u, 0u};
+  }
+  // their scale dwords (lanes 12..15 + 16 j) and the group-sum entries
+  // [g4][rt][16] that no conversion writes
+  for (int idx = tid; idx < nsp * RT * 16; idx += kThreads) {
+    const int j = idx & 3, r = 12 + ((idx >> 2) & 3), srt = idx >> 4;
+    const int sp = srt / RT, rt = srt - sp * RT;
+    reinterpret_cast<uint32_t*>(lds + sp * Lay::kSpan + Lay::kSc + rt * 256)[r + 16 * j] = 0x7f7f7f7fu;
+  }
+  for (int idx = tid; idx < nsp * 4 * RT * 16; idx += kThreads) {
+    const int e = idx & 15, rest = idx >> 4;  // rest = (sp * 4 + g4) * RT + rt
+    const int rt = rest % RT;
+    if (e >= 4 || 4 * rt + e >= a.M)
+      reinterpret_cast<float*>(lds + (rest / (4 * RT)) * Lay::kSpan + Lay::kXs)[(rest % (4 * RT)) * 16 + e] = 0.0f;
+  }
+  const int items = a.M * nsp * 16;
+  const int wi = tid & 15;
+  const int g4 = wi >> 2, b = wi & 3;
+  const int blk = 2 * g4 + (b >> 1);
+  const float inv_nsp = 1.0f / (float)nsp;
+#pragma unroll
+  for (int r = 0; r < kPrepRounds; ++r) {
+    if (r * kThreads >= items) break;  // uniform
+    const int it = tid + r * kThreads;
+    const bool valid = it < items;
+    const int ms = it >> 4;
+    const int m = (int)(((float)ms + 0.5f) * inv_nsp);
+    const int sp = ms - m * nsp;
+    uint32_t wd[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) wd[d] = L.q[r][d >> 2][d & 3];
+    uint32_t pc[3][4][2];
+    int sc[3];
+    float X;
+    q1_convert_word_bf8(wd, pc, sc, X);
+    X += dpp_xor1(X);
+    X += dpp_xor2(X);
+    if (valid) {
+      const int rt = m >> 2, i = m & 3;
+      unsigned char* base = lds + sp * Lay::kSpan;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int qa = 2 * (b & 1) + c;
+          *reinterpret_cast<u32x4*>(base + rt * Lay::kTileA + AL::chunk(blk, qa, 4 * p + i)) =
+              u32x4{pc[p][2 * c][0], pc[p][2 * c][1], pc[p][2 * c + 1][0], pc[p][2 * c + 1][1]};
+        }
+        base[Lay::kSc + rt * 256 + (4 * p + i + 16 * b) * 4 + g4] = (unsigned char)(sc[p] + 127);
+      }
+      if (b == 0) reinterpret_cast<float*>(base + Lay::kXs)[(g4 * RT + rt) * 16 + i] = X;
+    }
+  }
+}
+
 template <bool MBF16>
 __device__ __forceinline__ float meta_f32(uint32_t bits) {
   return MBF16 ? __uint_as_float(bits << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
@@ -263,6 +362,19 @@ __device__ __forceinline__ float meta_at(const uint32_t* v, int g) {
   return meta_f32<MBF16>(v[g]);
 }
 
+// One scaled MFMA for group g4 of a span (op_sel g4 picks the scale byte);
+// g4 is a constant after unrolling.  CBSZ: A format (0 fp8 E4M3, 1 bf8 E5M2);
+// B is fp4 (E2M1) with unit scales.
+template <int CBSZ>
+__device__ __forceinline__ v4f mfma_group(int g4, const v8i& A, const v8i& B, const v4f& C, uint32_t sa) {
+  switch (g4) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, CBSZ, 4, 0, (int)sa, 0, 0x7f7f7f7f);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, CBSZ, 4, 1, (int)sa, 0, 0x7f7f7f7f);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, CBSZ, 4, 2, (int)sa, 0, 0x7f7f7f7f);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, CBSZ, 4, 3, (int)sa, 0, 0x7f7f7f7f);
+  }
+}
+
 // Work.  Workgroup p of K segment `seg` owns tiles p, p + P, p + 2P, .. (16
 // rows each; consecutive tiles go to different workgroups) and the segment's
 // double spans (8 groups, 128 bytes of every row).  Its items (local tile k,
@@ -282,11 +394,13 @@ __device__ __forceinline__ float meta_at(const uint32_t* v, int g) {
 // dwords: the 8-byte writes and 4-byte reads are bank-conflict free).
 // MR: accumulator rows per lane quarter that can hold a live activation row
 // (1 for M = 1, 2 for M = 2, else 4); the others are never read, so their
-// scale multiply-adds are skipped.
-template <bool AFFINE, bool MBF16, bool PAIR, bool SC128, int MR>
+// scale multiply-adds are skipped.  RT (affine tensors): row tiles of 4
+// activation rows (1 for M <= 4, 2 for M = 5..8); symmetric tensors use one.
+template <bool AFFINE, bool MBF16, bool PAIR, bool SC128, int MR, int RT>
 __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
-  constexpr int RB = MR == 4 ? 8 : MR;  // A rows kept in LDS per half
+  constexpr int RB = (AFFINE || MR == 4) ? 8 : MR;  // symmetric: A rows kept in LDS per half
   using Lay = ALay<RB>;
+  constexpr int kSpanB = AFFINE ? AffLay<RT>::kSpan : Lay::kSpan;
   constexpr int NMAT = PAIR ? 2 : 1;
   // Ring slots (items in flight + those being computed).  Two: more items in
   // flight per wave congest the memory pipeline the waves issue into
@@ -311,8 +425,9 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   const int I = nbp * nds;                                          // items of this workgroup
   const int i0 = (wave * I) / kNW, i1 = ((wave + 1) * I) / kNW;
   const int nitems = i1 - i0;
-  float* red = reinterpret_cast<float*>(lds + (size_t)a.KSP * Lay::kSpan);  // [w][slot][mt][ab][64]
-  uint32_t* scr = reinterpret_cast<uint32_t*>(lds + (size_t)a.KSP * Lay::kSpan + (size_t)a.red_bytes) +
+  // [w][slot][mt][ab][64] (affine: [w][slot][mt][rt][64])
+  float* red = reinterpret_cast<float*>(lds + (size_t)a.KSP * kSpanB);
+  uint32_t* scr = reinterpret_cast<uint32_t*>(lds + (size_t)a.KSP * kSpanB + (size_t)a.red_bytes) +
                   wave * (NMAT * kScrDwords);
 
   const __amdgpu_buffer_rsrc_t rp[2] = {rsrc(a.p0, a.packed_bytes), rsrc(PAIR ? a.p1 : a.p0, a.packed_bytes)};
@@ -333,11 +448,11 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   u32x4 words[D][NMAT][2];
   uint32_t sreg[D][NMAT][NSC];
   uint32_t breg[D][NMAT][NSC];
-  float acc[NMAT][4];
+  float acc[NMAT][4 * RT];  // [mt][rt * 4 + i]
 #pragma unroll
   for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0f;
+    for (int i = 0; i < 4 * RT; ++i) acc[mt][i] = 0.0f;
 
   // issue the loads of item (local tile k, double span d) into slot u
   auto issue = [&](int u, int k, int d, bool ok) {
@@ -378,7 +493,10 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
     }
   };
   issue_next(0);
-  prep_compute<AFFINE, RB>(a, 2 * nds, lds, tid, pl);
+  if constexpr (AFFINE)
+    prep_compute_aff<RT>(a, 2 * nds, lds, tid, pl);
+  else
+    prep_compute<false, RB>(a, 2 * nds, lds, tid, pl);
 #pragma unroll
   for (int u = 1; u < D; ++u) issue_next(u);
   lds_barrier();
@@ -398,54 +516,91 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
 #pragma unroll
       for (int g = 0; g < 8; ++g) bw[mt][g] = t[nl * kScrStride + 4 * g + q];
     }
+    if constexpr (AFFINE) {
+      using AL = AffLay<RT>;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const unsigned char* base = lds + (2 * d + half) * Lay::kSpan;
-      const uint32_t scale_a = reinterpret_cast<const uint32_t*>(base + Lay::kSc)[lane];
-      v8i A[4];
-      v4f XS[4];
+      for (int half = 0; half < 2; ++half) {
+        const unsigned char* base = lds + (2 * d + half) * kSpanB;
+        uint32_t scale_a[RT];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        u32x4 h0, h1;
-        if (RB == 8) {
-          const int lane_sw = lane ^ q;  // position before the block's part of the swizzle
-          h0 = reinterpret_cast<const u32x4*>(base + a_blk_off(2 * g4))[lane_sw ^ ((g4 & 1) << 3)];
-          h1 = reinterpret_cast<const u32x4*>(base + a_blk_off(2 * g4 + 1))[lane_sw ^ (4 | ((g4 & 1) << 3))];
-        } else {
-          h0 = *reinterpret_cast<const u32x4*>(base + 2 * g4 * (128 * RB) + a_lane0);
-          h1 = *reinterpret_cast<const u32x4*>(base + (2 * g4 + 1) * (128 * RB) + a_lane0);
-        }
-        A[g4] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-        XS[g4] = reinterpret_cast<const v4f*>(base + Lay::kXs)[g4 * 4 + q];
-      }
-      const v4f zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt) {
-        v4f Dg[4];
+        for (int rt = 0; rt < RT; ++rt)
+          scale_a[rt] = reinterpret_cast<const uint32_t*>(base + AL::kSc + rt * 256)[lane];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const uint32_t wd = bw[mt][4 * half + g4];
-          const v8i B = {(int)(wd & 0x11111111u), (int)(wd & 0x22222222u), (int)(wd & 0x44444444u),
-                         (int)((wd >> 1) & 0x44444444u), 0, 0, 0, 0};
-          const v4f C = AFFINE ? zero : XS[g4];
-          if (g4 == 0)
-            Dg[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, C, 0, 4, 0, (int)scale_a, 0, 0x7f7f7f7f);
-          else if (g4 == 1)
-            Dg[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, C, 0, 4, 1, (int)scale_a, 0, 0x7f7f7f7f);
-          else if (g4 == 2)
-            Dg[2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, C, 0, 4, 2, (int)scale_a, 0, 0x7f7f7f7f);
-          else
-            Dg[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[3], B, C, 0, 4, 3, (int)scale_a, 0, 0x7f7f7f7f);
-        }
+          v8i A[RT];
+          v4f XS[RT];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float sv = meta_at<MBF16, SC128>(sreg[u][mt], 4 * half + g4);
+          for (int rt = 0; rt < RT; ++rt) {
+            const unsigned char* tb = base + rt * AL::kTileA;
+            const int lane_sw = lane ^ q;
+            const u32x4 h0 = reinterpret_cast<const u32x4*>(tb + a_blk_off(2 * g4))[lane_sw ^ ((g4 & 1) << 3)];
+            const u32x4 h1 = reinterpret_cast<const u32x4*>(tb + a_blk_off(2 * g4 + 1))[lane_sw ^ (4 | ((g4 & 1) << 3))];
+            A[rt] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+            XS[rt] = reinterpret_cast<const v4f*>(base + AL::kXs)[(g4 * RT + rt) * 4 + q];
+          }
 #pragma unroll
-          for (int i = 0; i < MR; ++i) acc[mt][i] = fmaf(sv, Dg[g4][i], acc[mt][i]);
-          if (AFFINE) {  // + b X
+          for (int mt = 0; mt < NMAT; ++mt) {
+            // weights of the two codes; the product runs over the code whose
+            // weight is larger in magnitude (d), the other enters through X
+            const float sv = meta_at<MBF16, SC128>(sreg[u][mt], 4 * half + g4);
             const float bv = meta_at<MBF16, SC128>(breg[u][mt], 4 * half + g4);
+            const float w1 = sv + bv;
+            const bool d1 = fabsf(w1) >= fabsf(bv);
+            const float dw = w1 - bv;
+            const float sd = d1 ? dw : -dw;  // w_d - w_o
+            const float wo = d1 ? bv : w1;
+            const uint32_t wd = bw[mt][4 * half + g4] ^ (d1 ? 0u : 0xffffffffu);
+            const v8i B = {(int)(wd & 0x11111111u), (int)(wd & 0x22222222u), (int)(wd & 0x44444444u),
+                           (int)((wd >> 1) & 0x44444444u), 0, 0, 0, 0};
+            const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < MR; ++i) acc[mt][i] = fmaf(bv, XS[g4][i], acc[mt][i]);
+            for (int rt = 0; rt < RT; ++rt) {
+              const v4f Dv = mfma_group<1>(g4, A[rt], B, zero, scale_a[rt]);
+#pragma unroll
+              for (int i = 0; i < MR; ++i) {
+                acc[mt][4 * rt + i] = fmaf(sd, Dv[i], acc[mt][4 * rt + i]);
+                acc[mt][4 * rt + i] = fmaf(wo, XS[rt][i], acc[mt][4 * rt + i]);
+              }
+            }
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const unsigned char* base = lds + (2 * d + half) * Lay::kSpan;
+        const uint32_t scale_a = reinterpret_cast<const uint32_t*>(base + Lay::kSc)[lane];
+        v8i A[4];
+        v4f XS[4];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          u32x4 h0, h1;
+          if (RB == 8) {
+            const int lane_sw = lane ^ q;  // position before the block's part of the swizzle
+            h0 = reinterpret_cast<const u32x4*>(base + a_blk_off(2 * g4))[lane_sw ^ ((g4 & 1) << 3)];
+            h1 = reinterpret_cast<const u32x4*>(base + a_blk_off(2 * g4 + 1))[lane_sw ^ (4 | ((g4 & 1) << 3))];
+          } else {
+            h0 = *reinterpret_cast<const u32x4*>(base + 2 * g4 * (128 * RB) + a_lane0);
+            h1 = *reinterpret_cast<const u32x4*>(base + (2 * g4 + 1) * (128 * RB) + a_lane0);
+          }
+          A[g4] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+          XS[g4] = reinterpret_cast<const v4f*>(base + Lay::kXs)[g4 * 4 + q];
+        }
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt) {
+          v4f Dg[4];
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const uint32_t wd = bw[mt][4 * half + g4];
+            const v8i B = {(int)(wd & 0x11111111u), (int)(wd & 0x22222222u), (int)(wd & 0x44444444u),
+                           (int)((wd >> 1) & 0x44444444u), 0, 0, 0, 0};
+            Dg[g4] = mfma_group<0>(g4, A[g4], B, XS[g4], scale_a);  // C = -X/2
+          }
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float sv = meta_at<MBF16, SC128>(sreg[u][mt], 4 * half + g4);
+#pragma unroll
+            for (int i = 0; i < MR; ++i) acc[mt][i] = fmaf(sv, Dg[g4][i], acc[mt][i]);
           }
         }
       }
@@ -472,18 +627,35 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   // activation row 4*((l>>4)&1) + 2*ab + (l>>5) of weight row l & 15 (hi + lo
   // combined); it goes to LDS slot (wave, k - first tile of the wave).
   const int kfirst = i0 / (nds > 0 ? nds : 1);
+  // Affine: quarter q of row tile rt holds piece q of activation rows
+  // 4 rt + i (element i); the four quarters are added (quarter 3 is zero),
+  // leaving activation row 4 rt + i in 16-lane row ((i & 1) << 1) | (i >> 1)
+  // of slot rt.
   auto tile_done = [&](int k) {
 #pragma unroll
     for (int mt = 0; mt < NMAT; ++mt) {
-      auto p01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[mt][0]), __float_as_uint(acc[mt][1]), false,
-                                                  false);
-      auto p23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[mt][2]), __float_as_uint(acc[mt][3]), false,
-                                                  false);
       float* slot = red + (((wave * a.TW + (k - kfirst)) * NMAT + mt) * 2) * 64 + lane;
-      slot[0] = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
-      slot[64] = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
+      if constexpr (AFFINE) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[mt][i] = 0.0f;
+        for (int rt = 0; rt < RT; ++rt) {
+          const float* v = &acc[mt][4 * rt];
+          auto p01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[1]), false, false);
+          auto p23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[2]), __float_as_uint(v[3]), false, false);
+          const float s01 = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
+          const float s23 = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
+          auto pp = __builtin_amdgcn_permlane16_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+          slot[64 * rt] = __uint_as_float(pp[0]) + __uint_as_float(pp[1]);
+        }
+      } else {
+        auto p01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[mt][0]), __float_as_uint(acc[mt][1]), false,
+                                                    false);
+        auto p23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[mt][2]), __float_as_uint(acc[mt][3]), false,
+                                                    false);
+        slot[0] = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
+        slot[64] = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4 * RT; ++i) acc[mt][i] = 0.0f;
     }
   };
 
@@ -537,7 +709,9 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
       wa = wa > kNW - 1 ? kNW - 1 : wa;
       while (wa > 0 && ((wa * I) >> 3) > t0) --wa;
       while (wa < kNW - 1 && (((wa + 1) * I) >> 3) <= t0) ++wa;
-      const int l = r + 16 * ((m >> 2) & 1) + 32 * (m & 1), ab = (m >> 1) & 1;
+      // position of (m, r) in the slots (see tile_done)
+      const int l = AFFINE ? r + 16 * (((m & 1) << 1) | ((m >> 1) & 1)) : r + 16 * ((m >> 2) & 1) + 32 * (m & 1);
+      const int ab = AFFINE ? (m >> 2) : (m >> 1) & 1;
       float v[NMAT];
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt) v[mt] = 0.0f;
@@ -553,15 +727,20 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   if (a.S == 1) return;
 
   // ---- split K: the last of the S workgroups with this p adds the
-  // partials of p's tiles in segment order ----
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are performed
-  lds_barrier();
+  // partials of p's tiles in segment order.  The workgroup's partial stores
+  // happen before the arrival (workgroup barrier, then an agent-scope release
+  // on the counter); the last arrival acquires at agent scope, and every
+  // wave that reads the partials acquires again after the barrier that
+  // hands it the flag. ----
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
+  __syncthreads();
   if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&a.counters[p], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(&a.counters[p], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     last_flag = old == (uint32_t)(a.S - 1);
   }
-  lds_barrier();
+  __syncthreads();
   if (!last_flag) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const int per_m = nbp * 16;
   const float inv_per_m = 1.0f / (float)per_m;
   for (int o = tid; o < per_m * a.M; o += kThreads) {
@@ -586,37 +765,35 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
   if (tid == 0) __hip_atomic_store(&a.counters[p], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-    else
-      cus = 256;
-  }
-  return cus;
-}
-
-template <bool AFFINE, bool MBF16, bool PAIR, bool SC128, int MR>
+template <bool AFFINE, bool MBF16, bool PAIR, bool SC128, int MR, int RT>
 hipError_t launch_k(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&q1_mma_kernel<AFFINE, MBF16, PAIR, SC128, MR>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&q1_mma_kernel<AFFINE, MBF16, PAIR, SC128, MR, RT>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 64);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((q1_mma_kernel<AFFINE, MBF16, PAIR, SC128, MR>), dim3((unsigned)p.wgs), dim3(kThreads),
+  hipLaunchKernelGGL((q1_mma_kernel<AFFINE, MBF16, PAIR, SC128, MR, RT>), dim3((unsigned)p.wgs), dim3(kThreads),
                      p.lds_bytes, s, a);
   return hipGetLastError();
 }
 
+// Live accumulator rows per lane quarter (MR) and affine row tiles (RT).
 template <bool AFFINE, bool MBF16, bool PAIR, bool SC128>
 hipError_t launch_r(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
-  if constexpr (PAIR) {
-    return launch_k<AFFINE, MBF16, PAIR, SC128, 4>(p, a, s);
+  if constexpr (AFFINE) {
+    if (a.M > 4) return launch_k<AFFINE, MBF16, PAIR, SC128, 4, 2>(p, a, s);
+    if constexpr (PAIR) {
+      return launch_k<AFFINE, MBF16, PAIR, SC128, 4, 1>(p, a, s);
+    } else {
+      if (a.M > 2) return launch_k<AFFINE, MBF16, PAIR, SC128, 4, 1>(p, a, s);
+      return a.M == 1 ? launch_k<AFFINE, MBF16, PAIR, SC128, 1, 1>(p, a, s)
+                      : launch_k<AFFINE, MBF16, PAIR, SC128, 2, 1>(p, a, s);
+    }
+  } else if constexpr (PAIR) {
+    return launch_k<AFFINE, MBF16, PAIR, SC128, 4, 1>(p, a, s);
   } else {
-    if (a.M > 2) return launch_k<AFFINE, MBF16, PAIR, SC128, 4>(p, a, s);
-    return a.M == 1 ? launch_k<AFFINE, MBF16, PAIR, SC128, 1>(p, a, s) : launch_k<AFFINE, MBF16, PAIR, SC128, 2>(p, a, s);
+    if (a.M > 2) return launch_k<AFFINE, MBF16, PAIR, SC128, 4, 1>(p, a, s);
+    return a.M == 1 ? launch_k<AFFINE, MBF16, PAIR, SC128, 1, 1>(p, a, s)
+                    : launch_k<AFFINE, MBF16, PAIR, SC128, 2, 1>(p, a, s);
   }
 }
 
@@ -628,7 +805,6 @@ hipError_t launch_t(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
 }  // namespace
 
 bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, const char** why) {
-  (void)affine;
   if (M < 1 || M > 8) {
     *why = "matrix-core packed path handles 1..8 activation rows";
     return false;
@@ -651,7 +827,7 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, c
   p->ntiles = (N + 15) / 16;
   const int ndsp = (p->nspan + 1) / 2;  // double spans
   const int rb = (pair || M > 2) ? 8 : M;
-  const size_t span = (size_t)span_bytes(rb);
+  const size_t span = affine ? (size_t)aff_span_bytes(M > 4 ? 2 : 1) : (size_t)span_bytes(rb);
   const size_t scratch = (size_t)kNW * nmat * kScrDwords * 4;
   const size_t budget = 160 * 1024 - 64;
   // Number of K segments S: among the splits whose LDS image, result slots

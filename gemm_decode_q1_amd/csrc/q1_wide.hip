@@ -6,11 +6,12 @@
 //
 // Two launches:
 //  * q1_act_image_kernel converts x once into a ready-to-load A operand image
-//    (see q1_fp8.h for the split x = hi + lo/16): per row block rb (16
-//    activation rows) and group g two 2 KB tiles (hi, lo) in MFMA lane order,
-//    [lane][32 B] (bytes 0..15 = k-half 0, 16..31 = k-half 1); per (rb, span
-//    of 4 groups) two E8M0 scale dwords per lane (hi, lo; byte g % 4); per
-//    (rb, g) 16 floats for the accumulator input (-X/2, or X for affine).
+//    (see q1_fp8.h): per row block rb (16 activation rows) and group g one
+//    2 KB tile per piece in MFMA lane order, [lane][32 B] (bytes 0..15 =
+//    k-half 0, 16..31 = k-half 1) -- symmetric tensors two fp8 pieces (hi,
+//    lo), affine ones three bf8 pieces; per (rb, span of 4 groups) one E8M0
+//    scale dword per piece and lane (byte g % 4); per (rb, g) 16 floats for
+//    the accumulator input (-X/2), or the group sums X for affine tensors.
 //  * q1_wide_kernel: a workgroup of 8 waves owns 8 row blocks (128 rows) and
 //    TNB * 16 weight rows; wave w owns row block w and all TNB column blocks,
 //    so its A operands come straight from the image, while the weights of
@@ -21,7 +22,11 @@
 //    scales, expands each word with one AND per bit class and chains two
 //    MFMAs per group through the accumulator input (hi, then lo with its own
 //    block scale), so the expansion and the group-scale multiply-add are paid
-//    once per 16 activation rows; b * X is added for affine tensors.
+//    once per 16 activation rows.  Affine tensors chain the three pieces and
+//    take, per weight row and group, the product over the code d whose weight
+//    is larger in magnitude (the word complemented when d = 0), adding
+//    (w_d - w_o) S_d + w_o X (as the narrow matrix-core kernel does, for the
+//    same reason: the error stays relative to sum |w x|).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -42,19 +47,6 @@ typedef float v2f_t __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowB = 80;  // LDS bytes per staged weight row: [4 words][4 groups] + pad
-
-int wide_device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-    else
-      cus = 256;
-  }
-  return cus;
-}
 
 template <bool MBF16>
 __device__ __forceinline__ float meta_val(uint32_t bits) {
@@ -85,10 +77,18 @@ __global__ __launch_bounds__(256) void q1_act_image_kernel(const uint16_t* __res
 #pragma unroll
     for (int d = 0; d < 16; ++d) wd[d] = 0u;  // rows past M: zero operands, zero sums
   }
-  uint32_t hi[4][2], lo[4][2];
-  int sc;
+  constexpr int NP = AFFINE ? 3 : 2;  // pieces
+  uint32_t pc[NP][4][2];
+  int sc[NP];
   float X;
-  q1_convert_word(wd, hi, lo, sc, X);
+  if constexpr (AFFINE) {
+    q1_convert_word_bf8(wd, pc, sc, X);
+  } else {
+    int s0;
+    q1_convert_word(wd, pc[0], pc[1], s0, X);
+    sc[0] = s0;
+    sc[1] = s0 - 4;  // lo = residual * 16
+  }
   X += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, X), 0xB1, 0xf, 0xf, false));
   X += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, X), 0x4E, 0xf, 0xf, false));
   if (g >= Gp) return;
@@ -96,19 +96,20 @@ __global__ __launch_bounds__(256) void q1_act_image_kernel(const uint16_t* __res
   const int ml = (int)(m & 15);
   // chunk (quarter qa = 2*(b & 1) + c, k-half b >> 1) of lane qa*16 + ml holds
   // in dword 2*(j & 1) + hh the class-j bytes of half word hh, j >> 1 == c
-  unsigned char* tile = img + (rb * Gp + g) * 4096 + (b >> 1) * 16;
+  unsigned char* tile = img + (rb * Gp + g) * (NP * 2048) + (b >> 1) * 16;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int qa = 2 * (b & 1) + c;
-    *reinterpret_cast<u32x4*>(tile + (qa * 16 + ml) * 32) =
-        u32x4{hi[2 * c][0], hi[2 * c][1], hi[2 * c + 1][0], hi[2 * c + 1][1]};
-    *reinterpret_cast<u32x4*>(tile + 2048 + (qa * 16 + ml) * 32) =
-        u32x4{lo[2 * c][0], lo[2 * c][1], lo[2 * c + 1][0], lo[2 * c + 1][1]};
+  for (int p = 0; p < NP; ++p) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int qa = 2 * (b & 1) + c;
+      *reinterpret_cast<u32x4*>(tile + p * 2048 + (qa * 16 + ml) * 32) =
+          u32x4{pc[p][2 * c][0], pc[p][2 * c][1], pc[p][2 * c + 1][0], pc[p][2 * c + 1][1]};
+    }
   }
   // scale of A row r, 32-weight block j (= word b) sits in lane r + 16 j
-  unsigned char* sp = sc_img + (rb * nspan + (g >> 2)) * 512 + (ml + 16 * b) * 4 + (g & 3);
-  sp[0] = (unsigned char)(sc + 127);
-  sp[256] = (unsigned char)(sc + 123);
+  unsigned char* sp = sc_img + (rb * nspan + (g >> 2)) * (NP * 256) + (ml + 16 * b) * 4 + (g & 3);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) sp[256 * p] = (unsigned char)(sc[p] + 127);
   if (b == 0) xs_img[(rb * Gp + g) * 16 + ml] = AFFINE ? X : -0.5f * X;
 }
 
@@ -142,14 +143,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kBufWord3);
 }
 
-// One group's two chained products for this lane: hi (accumulator input C)
-// then lo (accumulator input = the hi result), block scale byte BYTE of the
-// hi and lo scale dwords.
-template <int BYTE>
-__device__ __forceinline__ v4f mfma_hilo(const v8i& Ahi, const v8i& Alo, const v8i& B, const v4f& C, uint32_t shi,
-                                         uint32_t slo) {
-  const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Ahi, B, C, 0, 4, BYTE, (int)shi, 0, 0x7f7f7f7f);
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Alo, B, d, 0, 4, BYTE, (int)slo, 0, 0x7f7f7f7f);
+// One group's NP chained products for this lane: piece 0 (accumulator input
+// C), then each further piece with the previous result as accumulator input,
+// block scale byte BYTE of piece p's scale dword.  CBSZ: A format (0 fp8
+// E4M3, 1 bf8 E5M2); B fp4 with unit scales.
+template <int BYTE, int CBSZ, int NP>
+__device__ __forceinline__ v4f mfma_chain(const v8i (&A)[NP], const v8i& B, const v4f& C, const uint32_t (&sc)[NP]) {
+  v4f d = C;
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+    d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[p], B, d, CBSZ, 4, BYTE, (int)sc[p], 0, 0x7f7f7f7f);
+  return d;
 }
 
 template <bool AFFINE, bool MBF16, int TNB>
@@ -157,9 +161,14 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
   constexpr int ROWS = TNB * 16;                   // weight rows of the workgroup
   constexpr int LOADS = (ROWS * 4 + kThreads - 1) / kThreads;  // 16-byte staging loads per thread
   static_assert(ROWS <= kThreads, "one thread per staged row for the scales");
+  constexpr int NP = AFFINE ? 3 : 2;       // activation pieces (see q1_fp8.h)
   __shared__ __align__(16) unsigned char wsm[2][ROWS * kRowB];
-  __shared__ __align__(16) float ssm[2][ROWS * 4];  // the 4 group scales of each row, fp32
+  // per row and group, fp32: the scale (symmetric), or w_d - w_o (affine)
+  __shared__ __align__(16) float ssm[2][ROWS * 4];
+  // affine: w_o per row and group, and the code polarity (byte g = 0xff: the
+  // product runs over the clear bits, the word is complemented)
   __shared__ __align__(16) float bsm[AFFINE ? 2 : 1][AFFINE ? ROWS * 4 : 4];
+  __shared__ uint32_t pol[AFFINE ? 2 : 1][AFFINE ? ROWS : 1];
   __shared__ __align__(16) float xsm[2][kWaves * 4 * 16];  // group sums of a span: [row block][group][row]
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -232,35 +241,50 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
     }
     xsm[buf][tid] = xreg;
     if (tid < ROWS) {
-      *reinterpret_cast<v4f*>(&ssm[buf][4 * tid]) =
-          v4f{meta_val<MBF16>(sreg[0]), meta_val<MBF16>(sreg[0] >> 16), meta_val<MBF16>(sreg[1]),
-              meta_val<MBF16>(sreg[1] >> 16)};
-      if (AFFINE)
-        *reinterpret_cast<v4f*>(&bsm[buf][4 * tid]) =
-            v4f{meta_val<MBF16>(breg[0]), meta_val<MBF16>(breg[0] >> 16), meta_val<MBF16>(breg[1]),
-                meta_val<MBF16>(breg[1] >> 16)};
+      const v4f sv = v4f{meta_val<MBF16>(sreg[0]), meta_val<MBF16>(sreg[0] >> 16), meta_val<MBF16>(sreg[1]),
+                         meta_val<MBF16>(sreg[1] >> 16)};
+      if constexpr (AFFINE) {
+        const v4f bv = v4f{meta_val<MBF16>(breg[0]), meta_val<MBF16>(breg[0] >> 16), meta_val<MBF16>(breg[1]),
+                           meta_val<MBF16>(breg[1] >> 16)};
+        v4f sd, wo;
+        uint32_t pm = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {  // codes' weights w1 = s + b, w0 = b; d: the larger
+          const float w1 = sv[c] + bv[c];
+          const bool d1 = fabsf(w1) >= fabsf(bv[c]);
+          const float dw = w1 - bv[c];
+          sd[c] = d1 ? dw : -dw;
+          wo[c] = d1 ? bv[c] : w1;
+          pm |= d1 ? 0u : (0xffu << (8 * c));
+        }
+        *reinterpret_cast<v4f*>(&ssm[buf][4 * tid]) = sd;
+        *reinterpret_cast<v4f*>(&bsm[buf][4 * tid]) = wo;
+        pol[buf][tid] = pm;
+      } else {
+        *reinterpret_cast<v4f*>(&ssm[buf][4 * tid]) = sv;
+      }
     }
   };
 
   // ---- this wave's A operands: half span h (groups 4sp+2h, 4sp+2h+1) ----
-  // A[e][0] = hi, A[e][1] = lo of group 4sp+2h+e
-  auto a_load = [&](int sp, int h, v8i (&Ao)[2][2]) {
+  // A[e][p] = piece p of group 4sp+2h+e
+  auto a_load = [&](int sp, int h, v8i (&Ao)[2][NP]) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int g = 4 * sp + 2 * h + e;  // (groups past G are zero in the image)
 #pragma unroll
-      for (int hl = 0; hl < 2; ++hl) {
-        const u32x4* t = reinterpret_cast<const u32x4*>(a.img + ((int64_t)rb * (4 * a.nspan) + g) * 4096 +
-                                                        hl * 2048 + lane * 32);
+      for (int pp = 0; pp < NP; ++pp) {
+        const u32x4* t = reinterpret_cast<const u32x4*>(a.img + ((int64_t)rb * (4 * a.nspan) + g) * (NP * 2048) +
+                                                        pp * 2048 + lane * 32);
         const u32x4 h0 = t[0], h1 = t[1];
-        Ao[e][hl] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
+        Ao[e][pp] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
       }
     }
   };
-  auto sc_load = [&](int sp, uint32_t& shi, uint32_t& slo) {
-    const uint32_t* t = a.sc_img + ((int64_t)rb * a.nspan + sp) * 128 + lane;
-    shi = t[0];
-    slo = t[64];
+  auto sc_load = [&](int sp, uint32_t (&sc)[NP]) {
+    const uint32_t* t = a.sc_img + ((int64_t)rb * a.nspan + sp) * (NP * 64) + lane;
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) sc[pp] = t[64 * pp];
   };
 
   v4f acc[TNB];
@@ -268,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
   for (int j = 0; j < TNB; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // ---- products of half span h from LDS buffer buf ----
-  auto compute = [&](int buf, int h, const v8i (&A)[2][2], uint32_t shi, uint32_t slo) {
+  auto compute = [&](int buf, int h, const v8i (&A)[2][NP], const uint32_t (&sc)[NP]) {
     // groups past G (last span) have zero A operands, zero weights and zero
     // scales, so every span runs all its groups without branches
     v4f XS[2];  // this wave's group sums, rows 4q..4q+3
@@ -281,6 +305,7 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
     auto rd_b = [&](int j) {
       return AFFINE ? *reinterpret_cast<const v2f_t*>(&bsm[buf][4 * (j * 16 + nl) + 2 * h]) : v2f_t{0.f, 0.f};
     };
+    auto rd_pol = [&](int j) -> uint32_t { return AFFINE ? pol[buf][j * 16 + nl] : 0u; };
     auto fma_block = [&](int j, const v4f (&Dv)[2], v2f_t sv, v2f_t bv) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -294,28 +319,34 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
     };
     u32x2 w2n = rd_w(0);
     v2f_t s2n = rd_s(0), b2n = rd_b(0);
+    uint32_t pn = rd_pol(0);
     v4f Dp[2];
     v2f_t s2p = {0.f, 0.f}, b2p = {0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < TNB; ++j) {
       const u32x2 w2 = w2n;
       const v2f_t s2 = s2n, b2 = b2n;
+      const uint32_t pj = pn;
       if (j + 1 < TNB) {
         w2n = rd_w(j + 1);
         s2n = rd_s(j + 1);
         b2n = rd_b(j + 1);
+        pn = rd_pol(j + 1);
       }
       v4f D[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         int Bv[8];
-        q1_expand_b(w2[e], Bv);
+        // affine: complement the word when the product runs over the clear bits
+        const uint32_t wv = AFFINE ? w2[e] ^ (uint32_t)__builtin_amdgcn_sbfe((int)pj, 8 * (2 * h + e), 8) : w2[e];
+        q1_expand_b(wv, Bv);
         const v8i B = {Bv[0], Bv[1], Bv[2], Bv[3], 0, 0, 0, 0};
         const v4f C = AFFINE ? v4f{0.f, 0.f, 0.f, 0.f} : XS[e];
-        if (h == 0 && e == 0) D[e] = mfma_hilo<0>(A[e][0], A[e][1], B, C, shi, slo);
-        else if (h == 0) D[e] = mfma_hilo<1>(A[e][0], A[e][1], B, C, shi, slo);
-        else if (e == 0) D[e] = mfma_hilo<2>(A[e][0], A[e][1], B, C, shi, slo);
-        else D[e] = mfma_hilo<3>(A[e][0], A[e][1], B, C, shi, slo);
+        constexpr int CB = AFFINE ? 1 : 0;
+        if (h == 0 && e == 0) D[e] = mfma_chain<0, CB, NP>(A[e], B, C, sc);
+        else if (h == 0) D[e] = mfma_chain<1, CB, NP>(A[e], B, C, sc);
+        else if (e == 0) D[e] = mfma_chain<2, CB, NP>(A[e], B, C, sc);
+        else D[e] = mfma_chain<3, CB, NP>(A[e], B, C, sc);
       }
       // the scale multiply-adds of block j-1 go after block j's products,
       // so they never wait for a product just issued
@@ -334,12 +365,14 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
 
   // A0 holds the first half span's operands, A1 the second's; each loads
   // while the other half computes (no register copies between spans)
-  v8i A0[2][2], A1[2][2];
-  uint32_t shi = 0, slo = 0, shn = 0, sln = 0;
+  v8i A0[2][NP], A1[2][NP];
+  uint32_t scc[NP], scn[NP];
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) scc[pp] = scn[pp] = 0u;
   stage_load(0);
   if (live) {
     a_load(0, 0, A0);
-    sc_load(0, shi, slo);
+    sc_load(0, scc);
   }
   stage_store(0);
   lds_barrier();
@@ -350,17 +383,17 @@ __global__ __launch_bounds__(kThreads) void q1_wide_kernel(WideArgs a) {
     if (more) stage_load(sp + 1);
     if (live) {
       a_load(sp, 1, A1);
-      compute(buf, 0, A0, shi, slo);
+      compute(buf, 0, A0, scc);
       // (the next loads must not move above the products that read A0)
       __builtin_amdgcn_sched_barrier(0);
       {
         const int spn = more ? sp + 1 : 0;
         a_load(spn, 0, A0);
-        sc_load(spn, shn, sln);
+        sc_load(spn, scn);
       }
-      compute(buf, 1, A1, shi, slo);
-      shi = shn;
-      slo = sln;
+      compute(buf, 1, A1, scc);
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) scc[pp] = scn[pp];
     }
     if (more) stage_store(buf ^ 1);  // that buffer was last read before the previous barrier
     lds_barrier();
@@ -414,7 +447,7 @@ bool plan_wide(int64_t M, int64_t N, int64_t K, bool affine, WidePlan* p, const 
   p->mtiles = (p->MB + kWaves - 1) / kWaves;
   // column blocks per workgroup: the choice that keeps the most CUs busy in
   // the last round of workgroups (ties: the wider tile)
-  const int cus = wide_device_cus();
+  const int cus = device_cus();
   const int64_t nbk = (N + 15) / 16;
   const int cand[3] = {17, 16, 10};
   double best = -1.0;
@@ -429,8 +462,9 @@ bool plan_wide(int64_t M, int64_t N, int64_t K, bool affine, WidePlan* p, const 
       p->wgs = wgs;
     }
   }
-  const size_t img = (size_t)p->MB * p->nspan * 4 * 4096;
-  const size_t sc = (size_t)p->MB * p->nspan * 512;
+  const size_t np = affine ? 3 : 2;  // activation pieces per value
+  const size_t img = (size_t)p->MB * p->nspan * 4 * 2048 * np;
+  const size_t sc = (size_t)p->MB * p->nspan * 256 * np;
   const size_t xs = (size_t)p->MB * p->nspan * 4 * 64;
   p->sc_off = (img + 255) / 256 * 256;
   p->xs_off = p->sc_off + (sc + 255) / 256 * 256;

@@ -1,4 +1,4 @@
-"""Thin Python binding of ``libq1.so`` (see ``include/q1.h``).
+"""Thin Python binding of ``libq1.so`` (see ``include/q1.h`` and ``include/q1_measure.h``).
 
 Argument marshalling only: torch tensors provide device memory and the current
 stream; every operation runs in the library's HIP kernels.  There is no CPU or
@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libq1.so")
 Q1_F32, Q1_F16, Q1_BF16 = 0, 1, 2
 Q1_WS_RESERVED_BYTES = 16384  # arrival counters at the start of every workspace
 _TORCH_TO_Q1 = {torch.float32: Q1_F32, torch.float16: Q1_F16, torch.bfloat16: Q1_BF16}
-_STATUS = {0: "Q1_OK", 1: "Q1_ERR_INVALID_ARG", 2: "Q1_ERR_UNSUPPORTED", 3: "Q1_ERR_WORKSPACE", 4: "Q1_ERR_HIP"}
+_STATUS = {0: "Q1_OK", -1: "Q1_ERR_INVALID_ARG", -2: "Q1_ERR_UNSUPPORTED", -3: "Q1_ERR_WORKSPACE", -4: "Q1_ERR_HIP"}
+Q1_ERR_INVALID_ARG, Q1_ERR_UNSUPPORTED, Q1_ERR_WORKSPACE, Q1_ERR_HIP = -1, -2, -3, -4
 
 
 class Q1Error(RuntimeError):
@@ -171,7 +172,7 @@ def q1_qmm_workspace_bytes(M: int, w: PackedQ1) -> int:
     if n == 0 and load_library().q1_last_error():
         msg = load_library().q1_last_error().decode()
         if msg:
-            raise Q1Error(1, msg)
+            raise Q1Error(Q1_ERR_INVALID_ARG, msg)
     return n
 
 
@@ -179,9 +180,10 @@ _need_cache = {}
 
 
 def _qmm_need(L, M: int, w: PackedQ1, d: _Weight) -> int:
-    # (the wide-path choice follows Q1_WIDE_KERNEL, which the library reads
-    # on every call, so it is part of the key)
-    key = (M, w.N, w.K, d.meta_dtype, d.symmetric, os.environ.get("Q1_WIDE_KERNEL"))
+    # (the kernel choices follow Q1_WIDE_KERNEL and Q1_PACKED_KERNEL, which
+    # the library reads on every call, so they are part of the key)
+    key = (M, w.N, w.K, d.meta_dtype, d.symmetric, os.environ.get("Q1_WIDE_KERNEL"),
+           os.environ.get("Q1_PACKED_KERNEL"))
     n = _need_cache.get(key)
     if n is None:
         n = L.q1_qmm_workspace_bytes(M, ctypes.byref(d))

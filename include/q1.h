@@ -17,10 +17,14 @@
  *   - All tensor pointers are caller-owned device memory, contiguous and
  *     row-major.  The library keeps no reference after a call returns and never
  *     allocates device memory; temporaries live in a caller workspace.
- *   - Every call validates its arguments before any HIP call and returns
- *     Q1_ERR_INVALID_ARG / Q1_ERR_UNSUPPORTED / Q1_ERR_WORKSPACE with a short
- *     message in q1_last_error() (thread-local).  Q1_ERR_HIP reports a failed
- *     launch.  Kernel faults surface at the caller's next synchronisation.
+ *   - Every call checks shapes, dtypes, flags, pointers and alignment before
+ *     any HIP call.  The workspace check comes next: the size a call needs
+ *     depends on the device's compute-unit count, one attribute query cached
+ *     per device.  Then the current device is checked (gfx950).  Failures
+ *     return Q1_ERR_INVALID_ARG / Q1_ERR_UNSUPPORTED / Q1_ERR_WORKSPACE with a
+ *     short message in q1_last_error() (thread-local); Q1_ERR_HIP reports a
+ *     failed HIP call or launch.  Kernel faults surface at the caller's next
+ *     synchronisation.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *     work on it and return.
  *   - Rounding of every stored result is round-to-nearest-even; subnormals are
@@ -38,10 +42,10 @@ extern "C" {
 
 typedef enum q1_status {
   Q1_OK = 0,
-  Q1_ERR_INVALID_ARG = 1, /* a shape, pointer, dtype or flag is wrong */
-  Q1_ERR_UNSUPPORTED = 2, /* valid request this build does not serve (e.g. not gfx950) */
-  Q1_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the *_workspace_bytes query */
-  Q1_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+  Q1_ERR_INVALID_ARG = -1, /* a shape, pointer, dtype or flag is wrong */
+  Q1_ERR_UNSUPPORTED = -2, /* valid request this build does not serve (e.g. not gfx950) */
+  Q1_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than the *_workspace_bytes query */
+  Q1_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
 } q1_status;
 
 typedef enum q1_dtype { Q1_F32 = 0, Q1_F16 = 1, Q1_BF16 = 2 } q1_dtype;
@@ -172,17 +176,6 @@ q1_status q1_check_symmetric(const q1_weight* w, uint32_t* count, void* stream);
  */
 q1_status q1_pack_signs(const void* dense, int32_t dense_dtype, int64_t N, int64_t K, uint32_t* packed, void* scales,
                         int32_t meta_dtype, uint32_t* inexact, void* stream);
-
-/*
- * q1_stream_read -- measurement aid, not a step of the decode path: one pass
- * that reads `bytes` bytes at `data` with 16-byte non-temporal loads (the
- * access of the packed kernels) and computes nothing else.  Its duration is
- * the ceiling a single launch reading that many bytes can reach, the context
- * for the HBM rooflines of the other calls.
- *   data   device memory, 16-byte aligned; bytes a multiple of 16, < 2^31
- *   sink   device uint32, written only if the data XOR to a fixed sentinel
- */
-q1_status q1_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream);
 
 /* Largest M served by the packed kernel (1..8, default 8, initial value from
  * the environment variable Q1_QMM_MAX_ROWS).  Returns the previous value, or

@@ -10,13 +10,13 @@ import pytest
 from gemm_decode_q1_amd import q1 as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "q1.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include"))) if h.endswith(".h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libq1.so not built")
 
 
 def header_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(q1_[a-z0-9_]+)\s*\(", text)))
 
@@ -57,18 +57,18 @@ def qmm(w, M=1, x=FAKE, xd=B.Q1_BF16, y=FAKE, yd=B.Q1_F32, ws=None, wsb=0):
 
 
 @pytest.mark.parametrize("kw,code,msg", [
-    (dict(K=1000), 1, "multiple of 128"),
-    (dict(K=0), 1, "multiple of 128"),
-    (dict(N=0), 1, "N must be positive"),
-    (dict(group_size=64), 2, "group_size"),
-    (dict(reserved=3), 1, "reserved"),
-    (dict(meta_dtype=B.Q1_F32), 1, "metadata dtype"),
-    (dict(symmetric=1, biases=FAKE), 1, "must not carry biases"),
-    (dict(symmetric=0, biases=None), 1, "needs a biases pointer"),
-    (dict(symmetric=2), 1, "symmetric must be 0 or 1"),
-    (dict(packed=None), 1, "packed pointer is NULL"),
-    (dict(scales=None), 1, "scales pointer is NULL"),
-    (dict(packed=FAKE + 2), 1, "4-byte aligned"),
+    (dict(K=1000), -1, "multiple of 128"),
+    (dict(K=0), -1, "multiple of 128"),
+    (dict(N=0), -1, "N must be positive"),
+    (dict(group_size=64), -2, "group_size"),
+    (dict(reserved=3), -1, "reserved"),
+    (dict(meta_dtype=B.Q1_F32), -1, "metadata dtype"),
+    (dict(symmetric=1, biases=FAKE), -1, "must not carry biases"),
+    (dict(symmetric=0, biases=None), -1, "needs a biases pointer"),
+    (dict(symmetric=2), -1, "symmetric must be 0 or 1"),
+    (dict(packed=None), -1, "packed pointer is NULL"),
+    (dict(scales=None), -1, "scales pointer is NULL"),
+    (dict(packed=FAKE + 2), -1, "4-byte aligned"),
 ])
 def test_weight_validation(kw, code, msg):
     st, err = qmm(weight(**kw))
@@ -77,13 +77,13 @@ def test_weight_validation(kw, code, msg):
 
 def test_activation_validation():
     w = weight()
-    assert qmm(w, xd=B.Q1_F32)[0] == 2
-    assert qmm(w, M=-1)[0] == 1
-    assert qmm(w, yd=7)[0] == 1
+    assert qmm(w, xd=B.Q1_F32)[0] == -2
+    assert qmm(w, M=-1)[0] == -1
+    assert qmm(w, yd=7)[0] == -1
     st, err = qmm(w, x=FAKE + 8)
-    assert st == 1 and "16-byte aligned" in err
+    assert st == -1 and "16-byte aligned" in err
     st, err = qmm(w, x=0)
-    assert st == 1 and "NULL" in err
+    assert st == -1 and "NULL" in err
 
 
 def test_empty_batch_is_a_no_op():
@@ -96,9 +96,9 @@ def test_workspace_validation():
     need = L.q1_qmm_workspace_bytes(4, ctypes.byref(w))
     assert need > 0  # 4 rows, 17408 weights per row: a K split (partial sums + counters)
     st, err = qmm(w, M=4)
-    assert st == 3 and "workspace too small" in err
+    assert st == -3 and "workspace too small" in err
     st, err = qmm(w, M=4, ws=FAKE, wsb=need - 1)
-    assert st == 3
+    assert st == -3
     wide = L.q1_qmm_workspace_bytes(9, ctypes.byref(w))
     # 9 rows: two blocks of 8 rows, each 2 KB of fp8 operand per 128-weight group
     assert wide >= 2 * (17408 // 128) * 2048
@@ -107,11 +107,11 @@ def test_workspace_validation():
 def test_dequant_and_gather_validation():
     L = B.load_library()
     w = weight()
-    assert L.q1_dequantize(ctypes.byref(w), ctypes.c_void_p(FAKE), 9, None) == 1
-    assert L.q1_dequantize(ctypes.byref(w), None, B.Q1_BF16, None) == 1
-    assert L.q1_dequantize(ctypes.byref(weight(K=130)), ctypes.c_void_p(FAKE), B.Q1_BF16, None) == 1
-    assert L.q1_embed_rows(ctypes.c_void_p(FAKE), 2, 4, ctypes.byref(w), ctypes.c_void_p(FAKE), B.Q1_BF16, None) == 1
-    assert L.q1_embed_rows(ctypes.c_void_p(FAKE), 0, -1, ctypes.byref(w), ctypes.c_void_p(FAKE), B.Q1_BF16, None) == 1
+    assert L.q1_dequantize(ctypes.byref(w), ctypes.c_void_p(FAKE), 9, None) == -1
+    assert L.q1_dequantize(ctypes.byref(w), None, B.Q1_BF16, None) == -1
+    assert L.q1_dequantize(ctypes.byref(weight(K=130)), ctypes.c_void_p(FAKE), B.Q1_BF16, None) == -1
+    assert L.q1_embed_rows(ctypes.c_void_p(FAKE), 2, 4, ctypes.byref(w), ctypes.c_void_p(FAKE), B.Q1_BF16, None) == -1
+    assert L.q1_embed_rows(ctypes.c_void_p(FAKE), 0, -1, ctypes.byref(w), ctypes.c_void_p(FAKE), B.Q1_BF16, None) == -1
     assert L.q1_embed_rows(None, 0, 0, ctypes.byref(w), None, B.Q1_BF16, None) == 0  # T = 0
 
 
@@ -122,11 +122,11 @@ def test_ffn_validation():
     d = weight(N=512, K=512)  # K must equal gate.N = 256
     st = L.q1_ffn(ctypes.c_void_p(FAKE), 1, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), ctypes.c_void_p(FAKE),
                   None, 0, None)
-    assert st == 1 and "FFN shapes" in L.q1_last_error().decode()
+    assert st == -1 and "FFN shapes" in L.q1_last_error().decode()
     d = weight(N=512, K=256)
     st = L.q1_ffn(ctypes.c_void_p(FAKE), 1, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), ctypes.c_void_p(FAKE),
                   None, 0, None)
-    assert st == 3
+    assert st == -3
     assert L.q1_ffn_workspace_bytes(1, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d)) >= 256 * 2
 
 

@@ -74,7 +74,7 @@ def test_qmm_one_row_over_the_limit_is_rejected():
     for M in (1, 4):
         with pytest.raises(Q.Q1Error) as e:
             Q.q1_qmm(x.expand(M, K).contiguous(), W, torch.float32)
-        assert e.value.status == 2, str(e.value)
+        assert e.value.status == -2, str(e.value)
         assert "too large" in str(e.value)
     del packed, scales, W
     torch.cuda.empty_cache()

@@ -437,3 +437,17 @@ def test_planted_missing_bf16_rounding_is_caught(monkeypatch):
     _patch(monkeypatch, "qmm_ref", no_rounding)
     with pytest.raises(AssertionError):
         test_dense_bf16_bruteforce_and_bound(True, "f16")
+
+
+# ---------------------------------------------------------------- outlier inputs (GPU tolerance tests)
+
+def test_worked_outlier_case_has_the_hand_computed_result():
+    """Scale 0.25, bias -0.25: set bits weigh 0, clear bits -0.25; each
+    32-block contributes -0.25 * 16 * 2^-6 = -1/16, so K = 1024 gives -2
+    exactly, with sum |w x| = 2 (hand-worked)."""
+    from tests.outlier_inputs import worked_case
+    w, x = worked_case(1024, 3, False)
+    y, A = O.qmm_ref(x, w.packed, w.scales, w.biases, w.meta, False, w.K)
+    assert np.all(y == -2.0) and np.all(A == 2.0)
+    deq = O.dequant_f32(w.packed, w.scales, w.biases, w.meta, False, w.K)
+    assert set(np.unique(deq).tolist()) == {0.0, -0.25}
