@@ -39,29 +39,43 @@ def worked_case(K: int, N: int, clear_bits_small: bool):
     return S.Q1Weight(packed, scales, biases, "bf16", N, K), S.bf16_bits(x)
 
 
-def zero_weight_codes(rng, N: int, K: int, meta: str):
-    """Affine tensor whose groups cycle through three kinds: bias = -scale
-    (set bits weigh 0), bias = 0 (clear bits weigh 0) and a random bias.
-    Scales |N(0, 0.02)|; bits uniform."""
+def outlier_positions(rng, K: int) -> np.ndarray:
+    """One position per 32-weight block (shared by every activation row)."""
+    return np.arange(0, K, 32) + rng.integers(0, 32, size=K // 32)
+
+
+def zero_weight_codes(rng, N: int, K: int, meta: str, pos=None):
+    """Affine tensor whose groups alternate between bias = -scale (set bits
+    weigh 0) and bias = 0 (clear bits weigh 0); scales |N(0, 0.02)|, bits
+    uniform.  With ``pos`` (outlier positions), the bit at each position is
+    set to the code that weighs 0 in its group, so no outlier contributes to
+    sum |w x| and the tolerance holds only the other terms."""
     G = K // 128
     packed = rng.integers(0, 1 << 32, size=(N, K // 32), dtype=np.uint64).astype(np.uint32)
     sb = S.meta_bits(np.abs(rng.normal(0.0, 0.02, size=(N, G))).astype(np.float32), meta)
-    rb = S.meta_bits(rng.normal(0.0, 0.01, size=(N, G)).astype(np.float32), meta)
-    kind = (np.arange(N)[:, None] + np.arange(G)[None, :]) % 3
+    kind = (np.arange(N)[:, None] + np.arange(G)[None, :]) % 2
     # -scale exactly: the same bit pattern with the sign bit set
-    bb = np.where(kind == 0, sb ^ np.uint16(0x8000), np.where(kind == 1, np.uint16(0), rb)).astype(np.uint16)
+    bb = np.where(kind == 0, sb ^ np.uint16(0x8000), np.uint16(0)).astype(np.uint16)
+    if pos is not None:
+        for k in pos:
+            bit = np.uint32(1) << np.uint32(k & 31)
+            set_ = kind[:, k // 128] == 0
+            packed[set_, k >> 5] |= bit
+            packed[~set_, k >> 5] &= ~bit
     return S.Q1Weight(packed, sb, bb, meta, N, K)
 
 
-def outlier_x(rng, M: int, K: int, ratio_log2: int):
+def outlier_x(rng, M: int, K: int, ratio_log2: int, pos=None):
     """Activations N(0, 1) with, in every 32-block, one outlier of magnitude
-    2^ratio_log2 (times 1..2) and four elements scaled down by up to
-    2^-ratio_log2, so blocks span about 2^(2 ratio_log2)."""
+    2^ratio_log2 (times 1..2) -- at ``pos`` when given, else at a random
+    position per row -- and four elements scaled down by up to 2^-ratio_log2,
+    so blocks span about 2^(2 ratio_log2)."""
     x = rng.standard_normal((M, K)).astype(np.float32)
     for m in range(M):
         for w in range(K // 32):
-            j = 32 * w + int(rng.integers(32))
+            j = int(pos[w]) if pos is not None else 32 * w + int(rng.integers(32))
             x[m, j] = np.float32((1.0 + rng.random()) * 2.0 ** ratio_log2 * rng.choice([-1.0, 1.0]))
             small = 32 * w + rng.integers(32, size=4)
-            x[m, small] *= np.float32(2.0) ** -rng.integers(0, ratio_log2 + 1, size=4).astype(np.float32)
+            small = small[small != j]
+            x[m, small] *= np.float32(2.0) ** -rng.integers(0, ratio_log2 + 1, size=small.size).astype(np.float32)
     return S.bf16_bits(x)

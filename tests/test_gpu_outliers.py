@@ -15,7 +15,7 @@ import torch
 
 import oracle as O
 import q1_synth as S
-from tests.outlier_inputs import outlier_x, worked_case, zero_weight_codes
+from tests.outlier_inputs import outlier_positions, outlier_x, worked_case, zero_weight_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -64,11 +64,15 @@ def test_worked_case_zero_weight_outlier(M, clear_small):
 @pytest.mark.parametrize("ratio", [12, 14, 16])
 @pytest.mark.parametrize("sym", [False, True])
 def test_outlier_blocks(M, ratio, sym):
+    """Affine: every outlier sits on the code that weighs 0 in its group, so
+    the tolerance holds only the small terms; symmetric: all codes weigh
+    s/2."""
     rng = np.random.Generator(np.random.PCG64(900 + 7 * M + ratio + 100 * sym))
     N, K = 96, 2048
-    w = S.draw_weight(rng, N, K, "f16", True) if sym else zero_weight_codes(rng, N, K, "bf16")
-    x = outlier_x(rng, M, K, ratio)
-    _say(f"outliers 2^{ratio} M={M} {'sym' if sym else 'affine zero-weight codes'}")
+    pos = outlier_positions(rng, K)
+    w = S.draw_weight(rng, N, K, "f16", True) if sym else zero_weight_codes(rng, N, K, "bf16", pos)
+    x = outlier_x(rng, M, K, ratio, pos)
+    _say(f"outliers 2^{ratio} M={M} {'sym' if sym else 'affine, outliers on zero-weight codes'}")
     _check(w, x, f"2^{ratio} M={M} sym={sym}")
 
 
@@ -76,7 +80,8 @@ def test_outlier_blocks(M, ratio, sym):
 def test_outliers_affine_f16_long_rows(M):
     """K = 17408 (split K in the matrix-core kernel, several segments)."""
     rng = np.random.Generator(np.random.PCG64(77 + M))
-    w = zero_weight_codes(rng, 40, 17408, "f16")
-    x = outlier_x(rng, M, 17408, 14)
+    pos = outlier_positions(rng, 17408)
+    w = zero_weight_codes(rng, 40, 17408, "f16", pos)
+    x = outlier_x(rng, M, 17408, 14, pos)
     _say(f"outliers affine f16 K=17408 M={M}")
     _check(w, x, f"K=17408 M={M}")

@@ -451,3 +451,16 @@ def test_worked_outlier_case_has_the_hand_computed_result():
     assert np.all(y == -2.0) and np.all(A == 2.0)
     deq = O.dequant_f32(w.packed, w.scales, w.biases, w.meta, False, w.K)
     assert set(np.unique(deq).tolist()) == {0.0, -0.25}
+
+
+def test_adversarial_outlier_inputs_put_outliers_on_zero_weights():
+    """Every outlier of the GPU outlier tests meets a dequantised weight of
+    exactly 0, so the tolerance holds none of the outlier terms."""
+    from tests.outlier_inputs import outlier_positions, outlier_x, zero_weight_codes
+    rng = np.random.Generator(np.random.PCG64(1))
+    pos = outlier_positions(rng, 1024)
+    w = zero_weight_codes(rng, 6, 1024, "bf16", pos)
+    deq = O.dequant_f32(w.packed, w.scales, w.biases, "bf16", False, 1024)
+    assert np.all(deq[:, pos] == 0.0) and np.count_nonzero(deq) > deq.size // 3
+    x = O.bf16_to_f32(outlier_x(rng, 2, 1024, 12, pos))
+    assert np.all(np.abs(x[:, pos]) >= 2.0 ** 12)
