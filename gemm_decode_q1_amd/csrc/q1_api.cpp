@@ -269,6 +269,48 @@ q1_status run_packed(const PackedPlan& p, const uint16_t* x, int64_t x_ld, const
                     "packed kernel launch");
 }
 
+// Argument checks of q1_qmm and q1_qmm_noalloc (no HIP call).  *done: M == 0
+// (nothing to do).
+q1_status qmm_args(const void* x, int32_t x_dtype, int64_t M, const q1_weight* w, const void* y, int32_t y_dtype,
+                   bool* done) {
+  *done = false;
+  q1_status st = check_weight(w, "w");
+  if (st != Q1_OK) return st;
+  if (M < 0) return fail(Q1_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+  if (x_dtype != Q1_BF16) return fail(Q1_ERR_UNSUPPORTED, "x must be bf16");
+  if (!valid_out_dtype(y_dtype)) return fail(Q1_ERR_INVALID_ARG, "y dtype must be Q1_F32, Q1_F16 or Q1_BF16");
+  if (M == 0) {
+    *done = true;
+    return ok();
+  }
+  if (x == nullptr || y == nullptr) return fail(Q1_ERR_INVALID_ARG, "x and y must not be NULL");
+  if (!aligned(x, 16)) return fail(Q1_ERR_INVALID_ARG, "x must be 16-byte aligned");
+  if (!aligned(y, dtype_size(y_dtype))) return fail(Q1_ERR_INVALID_ARG, "y is misaligned");
+  return Q1_OK;
+}
+
+q1_status qmm_run(const void* x, int64_t M, const q1_weight* w, void* y, int32_t y_dtype, void* workspace,
+                  hipStream_t s) {
+  const q1::QMat a = to_mat(w);
+  auto* ws = static_cast<unsigned char*>(workspace);
+  if (M <= g_max_rows) {
+    PackedPlan p;
+    const char* why = "";
+    if (!plan_packed((int)M, w->N, w->K, false, !w->symmetric, &p, &why)) return fail(Q1_ERR_UNSUPPORTED, "%s", why);
+    return run_packed(p, static_cast<const uint16_t*>(x), w->K, a, nullptr, y, y_dtype, w->N, ws, kReserved, s);
+  }
+  q1::WidePlan wp;
+  const char* why = "";
+  if (use_wide_kernel() && q1::plan_wide(M, w->N, w->K, !w->symmetric, &wp, &why))
+    return hip_status(q1::launch_wide(wp, static_cast<const uint16_t*>(x), w->K, a, y, y_dtype, w->N, ws + kReserved, s),
+                      "wide launch");
+  uint16_t* deq = reinterpret_cast<uint16_t*>(ws + kReserved);
+  hipError_t e = q1::launch_dequant(a, nullptr, 0, w->N, deq, q1::BF16, s);
+  if (e != hipSuccess) return hip_status(e, "dequant launch");
+  return hip_status(q1::launch_gemm_bf16(static_cast<const uint16_t*>(x), deq, M, w->N, w->K, y, y_dtype, s),
+                    "gemm launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -323,40 +365,37 @@ size_t q1_qmm_workspace_bytes(int64_t M, const q1_weight* w) {
 
 q1_status q1_qmm(const void* x, int32_t x_dtype, int64_t M, const q1_weight* w, void* y, int32_t y_dtype,
                  void* workspace, size_t workspace_bytes, void* stream) {
-  q1_status st = check_weight(w, "w");
-  if (st != Q1_OK) return st;
-  if (M < 0) return fail(Q1_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
-  if (x_dtype != Q1_BF16) return fail(Q1_ERR_UNSUPPORTED, "x must be bf16");
-  if (!valid_out_dtype(y_dtype)) return fail(Q1_ERR_INVALID_ARG, "y dtype must be Q1_F32, Q1_F16 or Q1_BF16");
-  if (M == 0) return ok();
-  if (x == nullptr || y == nullptr) return fail(Q1_ERR_INVALID_ARG, "x and y must not be NULL");
-  if (!aligned(x, 16)) return fail(Q1_ERR_INVALID_ARG, "x must be 16-byte aligned");
-  if (!aligned(y, dtype_size(y_dtype))) return fail(Q1_ERR_INVALID_ARG, "y is misaligned");
+  bool done = false;
+  q1_status st = qmm_args(x, x_dtype, M, w, y, y_dtype, &done);
+  if (st != Q1_OK || done) return st;
   const size_t need = q1_qmm_workspace_bytes(M, w);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(Q1_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, workspace ? workspace_bytes : 0);
   if (need > 0 && !aligned(workspace, 256)) return fail(Q1_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   st = check_current_device();
   if (st != Q1_OK) return st;
+  return qmm_run(x, M, w, y, y_dtype, workspace, static_cast<hipStream_t>(stream));
+}
+
+q1_status q1_qmm_noalloc(const void* x, int32_t x_dtype, int64_t M, const q1_weight* w, void* y,
+                         int32_t y_dtype, void* stream) {
+  bool done = false;
+  q1_status st = qmm_args(x, x_dtype, M, w, y, y_dtype, &done);
+  if (st != Q1_OK || done) return st;
+  const size_t need = q1_qmm_workspace_bytes(M, w);
+  if (need > q1::kStaticScratchBytes)
+    return fail(Q1_ERR_WORKSPACE,
+                "this call needs %zu bytes of scratch; the static scratch holds %zu (use q1_qmm with a workspace)",
+                need, q1::kStaticScratchBytes);
+  st = check_current_device();
+  if (st != Q1_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const q1::QMat a = to_mat(w);
-  auto* ws = static_cast<unsigned char*>(workspace);
-  if (M <= g_max_rows) {
-    PackedPlan p;
-    const char* why = "";
-    if (!plan_packed((int)M, w->N, w->K, false, !w->symmetric, &p, &why)) return fail(Q1_ERR_UNSUPPORTED, "%s", why);
-    return run_packed(p, static_cast<const uint16_t*>(x), w->K, a, nullptr, y, y_dtype, w->N, ws, kReserved, s);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = q1::static_scratch(s, &ws);
+    if (e != hipSuccess) return hip_status(e, "static scratch set-up");
   }
-  q1::WidePlan wp;
-  const char* why = "";
-  if (use_wide_kernel() && q1::plan_wide(M, w->N, w->K, !w->symmetric, &wp, &why))
-    return hip_status(q1::launch_wide(wp, static_cast<const uint16_t*>(x), w->K, a, y, y_dtype, w->N, ws + kReserved, s),
-                      "wide launch");
-  uint16_t* deq = reinterpret_cast<uint16_t*>(ws + kReserved);
-  hipError_t e = q1::launch_dequant(a, nullptr, 0, w->N, deq, q1::BF16, s);
-  if (e != hipSuccess) return hip_status(e, "dequant launch");
-  return hip_status(q1::launch_gemm_bf16(static_cast<const uint16_t*>(x), deq, M, w->N, w->K, y, y_dtype, s),
-                    "gemm launch");
+  return qmm_run(x, M, w, y, y_dtype, ws, s);
 }
 
 q1_status q1_dequantize(const q1_weight* w, void* out, int32_t out_dtype, void* stream) {

@@ -33,6 +33,14 @@ constexpr int kCounterBytes = 16384;
 // Compute units of the current device (cached per device id).
 int device_cus();
 
+// Size of the library-owned device scratch that q1_qmm_noalloc uses instead
+// of a caller workspace (Q1_STATIC_SCRATCH_BYTES in the public header).
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+
+// Device address of the current device's static scratch (set up on the
+// first call on a device: symbol address, counters cleared on `stream`).
+hipError_t static_scratch(hipStream_t stream, void** ptr);
+
 struct QMat {
   const uint32_t* packed;
   const uint16_t* scales;

@@ -40,7 +40,7 @@ class _Weight(ctypes.Structure):
 _lib = None
 _lib_lock = threading.Lock()
 
-EXPORTS = ["q1_qmm", "q1_qmm_workspace_bytes", "q1_dequantize", "q1_embed_rows", "q1_ffn", "q1_ffn_workspace_bytes",
+EXPORTS = ["q1_qmm", "q1_qmm_noalloc", "q1_qmm_workspace_bytes", "q1_dequantize", "q1_embed_rows", "q1_ffn", "q1_ffn_workspace_bytes",
            "q1_check_symmetric", "q1_pack_signs", "q1_stream_read", "q1_set_max_packed_rows", "q1_device_supported", "q1_last_error",
            "q1_version"]
 
@@ -59,6 +59,7 @@ def load_library(path: str = LIB_PATH):
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         sig = {
             "q1_qmm": (i32, [vp, i32, i64, W, vp, i32, vp, sz, vp]),
+            "q1_qmm_noalloc": (i32, [vp, i32, i64, W, vp, i32, vp]),
             "q1_qmm_workspace_bytes": (sz, [i64, W]),
             "q1_dequantize": (i32, [W, vp, i32, vp]),
             "q1_embed_rows": (i32, [vp, i32, i64, W, vp, i32, vp]),
@@ -214,6 +215,25 @@ def q1_qmm(x: torch.Tensor, w: PackedQ1, out_dtype: torch.dtype = torch.bfloat16
                     ctypes.c_void_p(y.data_ptr()), _TORCH_TO_Q1.get(y.dtype, -1),
                     None if ws is None else ctypes.c_void_p(ws.data_ptr()), 0 if ws is None else ws.numel(),
                     _stream(x.device)))
+    return y
+
+
+def q1_qmm_noalloc(x: torch.Tensor, w: PackedQ1, out_dtype: torch.dtype = torch.bfloat16,
+                   y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``q1_qmm`` without a workspace: temporaries live in the library's own
+    device scratch (for callers that cannot allocate)."""
+    _check_tensor(x, "x")
+    if x.shape[-1] != w.K:
+        raise ValueError(f"x has {x.shape[-1]} features, weight has K={w.K}")
+    lead = tuple(x.shape[:-1])
+    M = math.prod(lead)
+    if y is None:
+        y = torch.empty(*lead, w.N, dtype=out_dtype, device=x.device)
+    _check_tensor(y, "y")
+    d = w.desc()
+    _check(load_library().q1_qmm_noalloc(ctypes.c_void_p(x.data_ptr()), _TORCH_TO_Q1.get(x.dtype, -1), M,
+                                         ctypes.byref(d), ctypes.c_void_p(y.data_ptr()),
+                                         _TORCH_TO_Q1.get(y.dtype, -1), _stream(x.device)))
     return y
 
 

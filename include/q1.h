@@ -98,6 +98,25 @@ q1_status q1_qmm(const void* x, int32_t x_dtype, int64_t M, const q1_weight* w, 
  * the call needs none).  Returns 0 and sets q1_last_error() on invalid input. */
 size_t q1_qmm_workspace_bytes(int64_t M, const q1_weight* w);
 
+/* Bytes of the library-owned device scratch used by q1_qmm_noalloc. */
+#define Q1_STATIC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * q1_qmm_noalloc -- q1_qmm for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, kernels and results as q1_qmm, without the
+ * workspace: temporaries live in a device array the library owns, one copy
+ * per GPU it runs on, Q1_STATIC_SCRATCH_BYTES large, held until the process
+ * ends.  Calls needing more (q1_qmm_workspace_bytes(M, w) above that size)
+ * fail with Q1_ERR_WORKSPACE.  The call allocates nothing.  The first call on
+ * a device sets the array up (its address, and a clearing kernel enqueued on
+ * `stream`).  All calls on one GPU share its array: calls that overlap on one
+ * GPU (different streams, no ordering) race; calls ordered on one stream do
+ * not.
+ */
+q1_status q1_qmm_noalloc(const void* x, int32_t x_dtype, int64_t M, const q1_weight* w, void* y, int32_t y_dtype,
+                         void* stream);
+
 /*
  * q1_dequantize -- out[N, K] = round(fl32(fl32(scale*bit) + bias)), bit-exact
  * (Higgs PR #212, "Walkthrough": Q1 dequantization kernel; rMLX #207,

@@ -143,3 +143,22 @@ def test_max_packed_rows_setter():
         assert L.q1_qmm_workspace_bytes(5, ctypes.byref(w)) >= (1024 // 128) * 2048
     finally:
         L.q1_set_max_packed_rows(prev)
+
+
+def test_noalloc_entry_validation():
+    """q1_qmm_noalloc checks its arguments, and rejects a call whose scratch
+    need exceeds the library's static array, before any HIP call."""
+    L = B.load_library()
+    w = weight(K=17408, N=5120)
+
+    def call(M, x=FAKE, y=FAKE, yd=B.Q1_BF16):
+        st = L.q1_qmm_noalloc(ctypes.c_void_p(x), B.Q1_BF16, M, ctypes.byref(w), ctypes.c_void_p(y), yd, None)
+        return st, L.q1_last_error().decode()
+
+    need = L.q1_qmm_workspace_bytes(512, ctypes.byref(w))
+    assert need > (8 << 20)
+    st, err = call(512)
+    assert st == -3 and "static scratch" in err
+    assert call(4, x=0)[0] == -1
+    assert call(4, yd=9)[0] == -1
+    assert call(0, x=0, y=0)[0] == 0
