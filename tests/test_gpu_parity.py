@@ -385,8 +385,7 @@ def _ffn_check(index, small, M, label, dense=False):
     _say(f"  y (on gpu h): worst ratio {ratio:.3e}")
     assert ok
     yb = O.ffn_y_bound(ref, wdict(d), weights_bf16=dense)
-    e2e = np.abs(O.out_to_f64(out_host(y), "bf16") - ref["y"])
-    assert (e2e <= yb).all()
+    assert O.check_within(out_host(y), "bf16", ref["y"], yb)[0]
 
 
 @pytest.mark.parametrize("M", list(range(1, 9)))
@@ -424,5 +423,4 @@ def test_ffn_mixed_formats(M, up_sym):
     ref = O.ffn_ref(x, wdict(g), wdict(u), wdict(d))
     dh = np.abs(O.bf16_to_f32(out_host(h)).astype(np.float64) - ref["h64"])
     assert (dh <= O.ffn_h_bound(ref)).all()
-    e2e = np.abs(O.out_to_f64(out_host(y), "bf16") - ref["y"])
-    assert (e2e <= O.ffn_y_bound(ref, wdict(d))).all()
+    assert O.check_within(out_host(y), "bf16", ref["y"], O.ffn_y_bound(ref, wdict(d)))[0]

@@ -464,3 +464,58 @@ def test_adversarial_outlier_inputs_put_outliers_on_zero_weights():
     assert np.all(deq[:, pos] == 0.0) and np.count_nonzero(deq) > deq.size // 3
     x = O.bf16_to_f32(outlier_x(rng, 2, 1024, 12, pos))
     assert np.all(np.abs(x[:, pos]) >= 2.0 ** 12)
+
+
+# ---------------------------------------------------------------- output rounding in the tolerance
+
+def test_output_half_ulp_hand_values():
+    """Half the spacing of the output grid at the stored value.  bf16 keeps 8
+    significant bits: 1.0 and 1.9921875 sit in [1, 2) with spacing 2^-7, 2.0
+    and -3.0 in [2, 4) with 2^-6; below 2^-126 the spacing is the subnormal
+    one, 2^-133 (so zero and every subnormal get 2^-134).  f32 outputs get
+    nothing: the fp32 accumulator is stored as it is."""
+    bf = O.f32_to_bf16_rne(np.array([1.0, 1.9921875, 2.0, -3.0, 0.0, 2.0 ** -126, 2.0 ** -130], np.float32))
+    assert O.output_half_ulp(bf, "bf16").tolist() == [2.0 ** -8, 2.0 ** -8, 2.0 ** -7, 2.0 ** -7, 2.0 ** -134,
+                                                      2.0 ** -134, 2.0 ** -134]
+    assert O.output_half_ulp(np.array([1.0, -7.5], np.float32), "f32").tolist() == [0.0, 0.0]
+
+
+def test_output_half_ulp_f16_matches_numpy_spacing():
+    """For binary16 the same quantity is half of NumPy's own float16 spacing
+    (a library routine) at every finite value below the largest."""
+    bits = np.arange(0, 0x7BFF, dtype=np.uint16)  # +0 .. the value below 65504
+    bits = np.concatenate([bits, bits | np.uint16(0x8000)])
+    want = np.spacing(np.abs(bits.view(np.float16))).astype(np.float64) / 2.0
+    assert np.array_equal(O.output_half_ulp(bits, "f16"), want)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_output_half_ulp_bounds_round_to_nearest(dtype):
+    """Brute force: every float32 value v, rounded to nearest even to the
+    output grid, lands within output_half_ulp(stored) of v -- and exact ties
+    (v halfway between two grid points) reach the bound, so it is tight."""
+    rng = np.random.Generator(np.random.PCG64(17))
+    mant = rng.integers(0, 1 << 23, size=200_000, dtype=np.uint32)
+    expo = rng.integers(127 - 30, 127 + 14, size=mant.size, dtype=np.uint32)
+    sign = rng.integers(0, 2, size=mant.size, dtype=np.uint32) << np.uint32(31)
+    v = (sign | (expo << np.uint32(23)) | mant).view(np.float32)
+    stored = O.round_to(v, dtype)
+    gap = np.abs(O.out_to_f64(stored, dtype) - v.astype(np.float64))
+    half = O.output_half_ulp(stored, dtype)
+    assert np.all(gap <= half)
+    assert np.any(gap == half)
+
+
+def test_check_close_allows_exactly_the_output_rounding():
+    """Hand case, bf16 output, sum |w x| = 1e-9 (tolerance about 1e-6): an
+    exact result of 1 + 2^-8 (a tie) stored as 1.0 passes (error = half an
+    ulp); 1 + 2^-8 + 1e-5 stored as 1.0 fails (it rounds to 1 + 2^-7); the
+    next grid value up also fails; a float32 output gets no rounding term."""
+    one = O.f32_to_bf16_rne(np.array([1.0], np.float32))
+    up = O.f32_to_bf16_rne(np.array([1.0 + 2.0 ** -7], np.float32))
+    A = np.array([1e-9])
+    assert O.check_close(one, "bf16", np.array([1.0 + 2.0 ** -8]), A)[0]
+    assert not O.check_close(one, "bf16", np.array([1.0 + 2.0 ** -8 + 1e-5]), A)[0]
+    assert not O.check_close(up, "bf16", np.array([1.0 + 2.0 ** -9]), A)[0]
+    assert not O.check_close(np.array([1.0], np.float32), "f32", np.array([1.0 + 2.0 ** -19]), A)[0]
+    assert O.check_close(np.array([1.0], np.float32), "f32", np.array([1.0 + 5e-7]), A)[0]
