@@ -59,7 +59,8 @@ def parse():
     return p.parse_args()
 
 
-ROWS = ["headline", "lm_head", "gather", "down", "dequant", "pack", "symcheck", "wide", "wide_dense", "ffn"]
+ROWS = ["headline", "lm_head", "gather", "down", "dequant", "pack", "symcheck", "wide", "wide_dense", "ffn",
+        "ffn_single"]
 
 
 def source_sha256() -> str:
@@ -288,7 +289,7 @@ def main():
             detail["check_symmetric_5120x17408_bf16"] = bw(sc_bytes, run_batch([lambda: Q.q1_check_symmetric(W3c)], 20))
             del W3c
 
-    if not args.quick and any(want(r) for r in ("dequant", "pack", "wide", "wide_dense", "ffn")):
+    if not args.quick and any(want(r) for r in ("dequant", "pack", "wide", "wide_dense", "ffn", "ffn_single")):
         wl5 = S.workload(5)
         g5 = wl5.weights["gate"]
         G5 = Q.PackedQ1.from_host(g5)
@@ -330,7 +331,7 @@ def main():
             detail["wide_M512_dense_fallback_5120x17408"] = {"us": round(us, 2), "TFLOP/s": round(tf, 1),
                                                              "pct_bf16_mfma": round(100 * tf / BF16_PEAK_TFLOPS, 1)}
             del wsd
-        if want("ffn"):
+        if want("ffn") or want("ffn_single"):
             # fused FFN, M=1..8 (three matrices, all symmetric fp16)
             FF = [Q.PackedQ1.from_host(wl5.weights[k]) for k in ("gate", "up", "down")]
             ffn_bytes = sum(wl5.weights[k].metric_bytes for k in ("gate", "up", "down"))
@@ -340,10 +341,23 @@ def main():
             yf = torch.empty(8, 5120, dtype=torch.bfloat16, device="cuda")
             wsf = {M: torch.zeros(max(Q.q1_ffn_workspace_bytes(M, *FF), 256), dtype=torch.uint8, device="cuda")
                    for M in Ms}
-            detail["fused_ffn_5120_17408_per_M"] = {
-                str(M): bw(ffn_bytes, run_batch(
-                    [(lambda F=F, M=M: Q.q1_ffn(x5[:M], *F, y=yf[:M], workspace=wsf[M])) for F in FFc], 2))
-                for M in Ms}
+            if want("ffn"):
+                detail["fused_ffn_5120_17408_per_M"] = {
+                    str(M): bw(ffn_bytes, run_batch(
+                        [(lambda F=F, M=M: Q.q1_ffn(x5[:M], *F, y=yf[:M], workspace=wsf[M])) for F in FFc], 2))
+                    for M in Ms}
+            if want("ffn_single"):
+                # the same FFN as one persistent launch (Q1_FFN_KERNEL=single)
+                os.environ["Q1_FFN_KERNEL"] = "single"
+                try:
+                    wss = {M: torch.zeros(max(Q.q1_ffn_workspace_bytes(M, *FF), 256), dtype=torch.uint8,
+                                          device="cuda") for M in Ms}
+                    detail["ffn_single_launch_5120_17408_per_M"] = {
+                        str(M): bw(ffn_bytes, run_batch(
+                            [(lambda F=F, M=M: Q.q1_ffn(x5[:M], *F, y=yf[:M], workspace=wss[M])) for F in FFc], 2))
+                        for M in Ms}
+                finally:
+                    del os.environ["Q1_FFN_KERNEL"]
             del FFc
         torch.cuda.synchronize()
 

@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libq1.so")
 SOURCES = ([os.path.join(PKG, "csrc", "q1_api.cpp"), os.path.join(PKG, "csrc", "q1_kernels.hip"),
-            os.path.join(PKG, "csrc", "q1_mma.hip"), os.path.join(PKG, "csrc", "q1_wide.hip"),
+            os.path.join(PKG, "csrc", "q1_mma.hip"), os.path.join(PKG, "csrc", "q1_ffn.hip"),
+            os.path.join(PKG, "csrc", "q1_wide.hip"),
             os.path.join(PKG, "csrc", "q1_meta.hip"), os.path.join(PKG, "csrc", "q1_scratch.hip")] +
            [os.path.join(PKG, "csrc", f"q1_gemv_m{m}.hip") for m in range(1, 9)])
 # Packed-FP32 instructions are disabled for all device code (see the design

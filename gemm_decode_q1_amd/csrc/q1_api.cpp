@@ -140,6 +140,16 @@ bool use_wide_kernel() {
   return !(e && strcmp(e, "dequant") == 0);
 }
 
+// Packed FFN: Q1_FFN_KERNEL=single runs gate/up, SiLU*mul and down in one
+// persistent launch when the three matrices are of one kind (q1_ffn.hip);
+// otherwise the pair launch, then the down launch, which is faster on MI355X
+// (the single launch's agent-scope release of h is an L2 writeback that waits
+// behind the weight stream).  Read on every call and by the workspace query.
+bool ffn_single_enabled() {
+  const char* e = getenv("Q1_FFN_KERNEL");
+  return e && strcmp(e, "single") == 0;
+}
+
 struct PackedPlan {
   bool table;
   q1::GemvPlan g;
@@ -190,6 +200,9 @@ PackedWs packed_ws(const PackedPlan& p, size_t base) {
 
 struct FfnWs {
   bool packed, fused;
+  bool single;                     // one persistent launch (q1_ffn.hip)
+  q1::FfnPlan fp;
+  size_t part_off;                 // single: down split-K partials
   PackedPlan pgu, pg, pu, pd;
   size_t h_off, gu_off, d_off;     // packed: counters+partials blocks
   size_t g_off, u_off;             // unfused / wide: fp32 g and u
@@ -211,6 +224,13 @@ q1_status ffn_layout(int64_t M, const q1_weight* gate, const q1_weight* up, cons
   L->h_off = kReserved;
   size_t off = align_up(kReserved + (size_t)M * I * 2, 256);
   const char* why = "";
+  L->single = L->fused && ffn_single_enabled() && down->symmetric == gate->symmetric &&
+              down->meta_dtype == gate->meta_dtype && q1::plan_ffn((int)M, I, H, Ho, !gate->symmetric, &L->fp, &why);
+  if (L->single) {
+    L->part_off = off;
+    L->bytes = align_up(off + L->fp.d.partial_floats * sizeof(float), 256);
+    return Q1_OK;
+  }
   if (L->packed) {
     if (L->fused) {
       if (!plan_packed((int)M, I, H, true, !gate->symmetric, &L->pgu, &why)) return fail(Q1_ERR_UNSUPPORTED, "%s", why);
@@ -515,6 +535,10 @@ q1_status q1_ffn(const void* x, int64_t M, const q1_weight* gate, const q1_weigh
   const auto* xb = static_cast<const uint16_t*>(x);
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h_off);
   const q1::QMat g = to_mat(gate), u = to_mat(up), d = to_mat(down);
+  if (L.single)
+    return hip_status(q1::launch_ffn(L.fp, xb, g, u, d, h, y, reinterpret_cast<float*>(ws + L.part_off),
+                                     reinterpret_cast<uint32_t*>(ws), s),
+                      "FFN launch");
   if (L.packed) {
     if (L.fused) {
       st = run_packed(L.pgu, xb, H, g, &u, h, Q1_BF16, I, ws, L.gu_off, s);

@@ -137,9 +137,43 @@ struct MmaArgs {
 };
 
 bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* plan, const char** why);
+// The plan for a given split: S K segments of P workgroups each (P is
+// capped at the tile count).  False when S is not a distinct split of K or
+// the segment's LDS image, result slots and scratch do not fit.
+bool plan_mma_split(int M, int64_t N, int64_t K, bool pair, bool affine, int S, int64_t P, MmaPlan* plan);
+
+// Kernel arguments of one matrix-core stage (plan + operands).
+MmaArgs mma_args(const MmaPlan& plan, const uint16_t* x, int64_t x_ld, const QMat& a, const QMat* b, void* out,
+                 int32_t out_dtype, int64_t out_ld, float* partial, uint32_t* counters);
 
 hipError_t launch_mma(const MmaPlan& plan, const uint16_t* x, int64_t x_ld, const QMat& a, const QMat* b, void* out,
                       int32_t out_dtype, int64_t out_ld, float* partial, uint32_t* counters, hipStream_t stream);
+
+// ---- single-launch FFN (q1_ffn.hip) ----------------------------------------
+
+// One persistent launch of one workgroup per compute unit: phase 1 is the
+// gate/up pair (whole K per workgroup, h written as bf16), phase 2 the down
+// projection split into K segments, each waiting for the phase-1 tiles that
+// produce its part of h.
+struct FfnPlan {
+  MmaPlan gu;   // phase 1 (S = 1, P = its workgroups)
+  MmaPlan d;    // phase 2 (S segments x P workgroups)
+  int64_t wgs;  // grid
+  size_t lds_bytes;
+  int sync_words;  // uint32 words of the counter block in use (split-K, segment and exit counters)
+};
+
+// Status word of the single-launch FFN: the last uint32 of the counter block
+// at the start of the workspace.
+constexpr int kFfnStatusWord = kCounterBytes / 4 - 1;
+
+bool plan_ffn(int M, int64_t I, int64_t H, int64_t Ho, bool affine, FfnPlan* plan, const char** why);
+
+// gate, up and down share symmetry and metadata dtype.  h: bf16 [M, I];
+// y: bf16 [M, Ho]; partial: plan.d.partial_floats floats; sync: the
+// workspace's counter block (zero on entry, zero again on exit).
+hipError_t launch_ffn(const FfnPlan& plan, const uint16_t* x, const QMat& gate, const QMat& up, const QMat& down,
+                      uint16_t* h, void* y, float* partial, uint32_t* sync, hipStream_t stream);
 
 // Returns false (with a message) when the request cannot be planned.
 bool plan_gemv(int M, int64_t N, int64_t K, bool pair, bool affine, GemvPlan* plan, const char** why);

@@ -1,771 +1,23 @@
-// Packed narrow-M Q1 matmul on the CDNA4 matrix cores.
-//
-//   y[m][n] = sum_k x[m][k] * w[n][k],   w = s*bit + b   (symmetric: b = -s/2)
-//
-// for M <= 8 activation rows, straight from the packed weights (Higgs PR #212,
-// "What": narrow Q1 matmuls stay packed; rMLX issue #207 for the format: 32
-// weights per uint32, LSB first, one scale and bias per 128 weights).
-//
-// Per weight row n and group g of 128 weights
-//   sum_k w x = s*S + b*X,   S = sum_k bit_k x_k,   X = sum_k x_k
-// (symmetric: s*(S - X/2)).  S is the product of a 0/1 matrix with the
-// activations, and that product runs on v_mfma_scale_f32_16x16x128_f8f6f4:
-//
-// * B operand: the bits of one packed word per lane, expanded to fp4 (E2M1)
-//   codes by bit class j (bits 4i+j of the word, nibble i): classes 0, 1, 2
-//   keep their bit in place (codes 0.5, 1 and 2 for a set bit, 0 for a clear
-//   one: one AND each) and class 3 moves its bit to position 2 (code 2).  The
-//   activations of class j are pre-multiplied by 1/code (2, 1, 1/2, 1/2, all
-//   powers of two, so exact), which makes each MFMA compute
-//   D = S = sum of x over the set bits of the group.  Then
-//     symmetric: sum w x = s (S - X/2),  affine: sum w x = s S + b X,
-//   with X the group sum of x: for symmetric tensors -X/2 enters as the
-//   MFMA's accumulator input, for affine ones b X is added after it.
-// * A operand, symmetric tensors: each activation as two fp8 (E4M3) pieces,
-//   x = hi + lo/16, with one power-of-two block scale per 32 weights chosen
-//   from the block's largest |x|.  A bf16 value has 8 significant bits, hi
-//   carries the top 4 (rounded) and lo the rest, so the pair is exact for
-//   every element within 2^11 of its block's largest magnitude; below that
-//   the error is at most 2^-19 of the block maximum, and since every weight
-//   of a symmetric group has the same magnitude s/2, the product's error
-//   stays below 2^-14 s sum|x| -- an eighth of the tolerance.  Rows 0..7 of
-//   the 16-row A tile hold hi for the M activation rows and rows 8..15 hold
-//   lo; the two halves of the result are added at the end.
-// * Affine tensors: the weights of a group are w1 = fl(s + b) (set bits) and
-//   w0 = b (clear bits), of any relative size, so an error relative to the
-//   block's largest |x| is not relative to sum |w x|.  Two changes make it so:
-//   (1) each activation is split into three E5M2 (bf8) pieces with their own
-//   block scales, exact for every element within 2^25 of its block maximum
-//   (q1_fp8.h); piece p of activation row m is A row 4p + m % 4 of row tile
-//   m / 4 (rows 12..15 hold zeros); (2) per weight row and group the product
-//   runs over the code class d whose weight is larger in magnitude (the B
-//   word is complemented when d = 0), and the group's contribution is
-//     (w_d - w_o) S_d + w_o X,   S_d = sum of x over the codes equal to d,
-//   so the rounding of X and of the fp32 sums is multiplied by the smaller
-//   weight w_o, and S_d's error by 2 |w_d|, both within the tolerance.
-// * One instruction covers 16 weight rows x one group (128 weights): its fp32
-//   result is multiplied by the group scale (and the bias term added) on the
-//   vector ALU.
-//
-// Operand layouts of the instruction (gfx950, fp8 A / fp4 B):
-//   A lane l: row l%16; byte e holds k-index 16*(l/16) + e (e < 16) or
-//             64 + 16*(l/16) + e - 16 (e >= 16); the scale of (row r, 32-k
-//             block j) is in lane r + 16*j, byte op_sel.
-//   B lane l: column l%16; code e (dword e/8, nibble e%8) holds k-index
-//             32*(l/16) + e, so lane l/16 = q carries word q of the group.
-//   D lane l: column l%16, rows 4*(l/16) .. +3.
-//
-// Work decomposition.  A workgroup (8 waves) owns a block of row tiles (16
-// rows each) and a segment of K (spans of 4 groups).  First every thread
-// converts the segment's activations into the A operand image in LDS; then
-// wave (ws, wt) takes spans ws, ws+NWS.. of the segment and tiles wt, wt+NWT..
-// of the block.  A lane loads 16 bytes = one group's 4 words of one row; a
-// 4x4 transpose across the lane quarters (two permlane32 and two permlane16
-// swaps) gives lane quarter q word q of each of the 4 groups.  The waves'
-// partial sums meet in LDS and are added in a fixed order.  With more than one
-// K segment (grid split), each segment writes fp32 partials with agent-scope
-// stores and the last workgroup to finish a row block adds them in segment
-// order, so results never depend on timing.
+// Packed narrow-M Q1 matmul on the CDNA4 matrix cores: one launch of the
+// stage in q1_mma_stage.h (which describes the scheme), its plan and its
+// launch.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdint>
 
-#include "q1_device.h"
-#include "q1_fp8.h"
-#include "q1_internal.h"
+#include "q1_mma_stage.h"
 
 namespace q1 {
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kNW = 8;  // waves per workgroup
-constexpr int kThreads = kNW * 64;
-
-// LDS image of one span (4 groups): A operand [g4][half][64 lanes][16 B],
-// block scales [64 lanes][4 groups] bytes, and the group sums of the
-// activations [g4][16 D rows] floats (-X/2 for symmetric tensors, X for
-// affine; zero for the lo rows 8..15 and rows of activation index >= M).
-// With RB = 8 (any M) each 1 KB block (g4, half) stores the 16-byte chunk of
-// lane 16*qa + row at position 16*qa + (row ^ a_swz(qa, block)), and the
-// blocks of group g4 start 16*g4 bytes late: reads of 8 (or 16) consecutive
-// lanes still cover distinct banks, and the conversion's chunk writes (one
-// activation row per 16 lanes) spread over the banks too.  With RB = 1 or 2
-// (M = 1 or 2) only the live rows are stored: hi rows 0..RB-1 and lo rows
-// 8..8+RB-1, 2*RB chunks per quarter; the lanes of the other rows read the
-// chunk of row (row & (RB-1)) of their half (an LDS broadcast), which only
-// reaches MFMA result rows that are never read.  The smaller image lets one
-// workgroup hold a longer K segment.
-__device__ __forceinline__ int a_blk_off(int blk) { return blk * 1024 + (blk >> 1) * 16; }
-__device__ __forceinline__ int a_swz(int qa, int blk) { return qa | ((blk & 3) << 2); }
-
-template <int RB>
-struct ALay {
-  static constexpr int kA = RB == 8 ? 4 * 2064 : 1024 * RB;  // A operand bytes
-  static constexpr int kSc = kA;                              // block scales
-  static constexpr int kXs = kA + 256;                        // group sums
-  static constexpr int kSpan = kA + 512;                      // one span
-  // byte offset of the chunk of (block, quarter qa, tile row r); r is a live
-  // row for the writer, any row for a reader
-  static __device__ __forceinline__ int chunk(int blk, int qa, int r) {
-    if (RB == 8) return a_blk_off(blk) + (qa * 16 + (r ^ a_swz(qa, blk))) * 16;
-    return blk * (128 * RB) + (qa * 2 * RB + (r & (RB - 1)) + RB * (r >> 3)) * 16;
-  }
-};
-constexpr int span_bytes(int rb) { return rb == 8 ? 4 * 2064 + 512 : 1024 * rb + 512; }
-
-// LDS image of one span for affine tensors (RT row tiles of 4 activation
-// rows): per row tile an A operand image laid out as ALay<8> (rows 4p + i:
-// piece p of activation row 4 rt + i; rows 12..15 zero), the block scales
-// [rt][64 lanes][4 groups] bytes, and the group sums [g4][rt][16] floats (X of
-// activation row 4 rt + i in entry i for the piece-0 lanes, zero in entries
-// 4..15, so only one quarter of the result adds w_o X).
-template <int RT>
-struct AffLay {
-  static constexpr int kTileA = 4 * 2064;
-  static constexpr int kA = RT * kTileA;
-  static constexpr int kSc = kA;
-  static constexpr int kXs = kA + RT * 256;
-  static constexpr int kSpan = kA + RT * 512;
-};
-constexpr int aff_span_bytes(int rt) { return rt * (4 * 2064 + 512); }
-
-// per-wave LDS scratch of the word transpose: 16 rows x 34 dwords (32 used)
-constexpr int kScrStride = 34;
-constexpr int kScrDwords = 16 * kScrStride;
-
-constexpr uint32_t kBufWord3 = 0x00020000u;
-constexpr uint32_t kOOB = 0x80000000u;
-// cache policy of loads read once per launch (packed words, scales, biases):
-// non-temporal (scales with it measured 1-3 % faster at K=5120, N=17408)
-constexpr int kNTLoad = 2;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kBufWord3);
-}
-
-__device__ __forceinline__ float dpp_xor1(float v) {  // quad_perm [1,0,3,2]
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float dpp_xor2(float v) {  // quad_perm [2,3,0,1]
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xf, 0xf, false));
-}
-
-
-// Conversion of the activations of spans [span0, span0 + nsp) into the LDS
-// image.  Item = (row m, span, word): the 32 activations of one packed word's
-// weights, giving for the hi and the lo piece the two 16-byte A chunks of the
-// word (bit classes 0,1 and 2,3).  The loads of all of a thread's items (at
-// most kPrepRounds) are issued first (prep_load), so they can be in flight
-// together with the weight loads issued right after them.
-constexpr int kPrepRounds = 4;
-
-struct PrepLoads {
-  u32x4 q[kPrepRounds][4];
-};
-
-__device__ __forceinline__ void prep_load(const MmaArgs& a, int span0, int nsp, int tid, PrepLoads& L) {
-  const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, a.x_bytes);
-  const int items = a.M * nsp * 16;
-  const float inv_nsp = 1.0f / (float)nsp;
-#pragma unroll
-  for (int r = 0; r < kPrepRounds; ++r) {
-    const int it = tid + r * kThreads;
-    const bool valid = it < items;
-    const int wi = it & 15, ms = it >> 4;
-    const int m = (int)(((float)ms + 0.5f) * inv_nsp);  // ms / nsp (exact: ms < 2^20)
-    const int sp = ms - m * nsp;
-    const int k0 = (span0 + sp) * 512 + wi * 32;
-    const uint32_t off = (uint32_t)(((int64_t)m * a.x_ld + k0) * 2) | ((valid && k0 < a.K) ? 0u : kOOB);
-    if (r * kThreads < items) {  // uniform: skip rounds nobody needs
-#pragma unroll
-      for (int c = 0; c < 4; ++c) L.q[r][c] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16 * c, 0, 0);
-    }
-  }
-}
-
-template <bool AFFINE, int RB>
-__device__ void prep_compute(const MmaArgs& a, int nsp, unsigned char* lds, int tid, const PrepLoads& L) {
-  using Lay = ALay<RB>;
-  // A rows of activation index >= M and their scales are never written: the
-  // MFMA keeps rows apart, so whatever they hold only reaches result rows that
-  // are never read.  The group sums enter as the accumulator input of every
-  // row and must be zero for the lo rows 8..15 (and are for rows >= M).
-  for (int idx = tid; idx < nsp * 64; idx += kThreads) {  // [g4][16] sums
-    if ((idx & 15) >= a.M) reinterpret_cast<float*>(lds + (idx >> 6) * Lay::kSpan + Lay::kXs)[idx & 63] = 0.0f;
-  }
-  const int items = a.M * nsp * 16;
-  // item = tid + 512 r: the word wi does not depend on the round; the (row,
-  // span) index ms = tid/16 + 32 r is split by a rounded reciprocal
-  const int wi = tid & 15;
-  const int g4 = wi >> 2, b = wi & 3;
-  const int blk = 2 * g4 + (b >> 1);
-  const float inv_nsp = 1.0f / (float)nsp;
-#pragma unroll
-  for (int r = 0; r < kPrepRounds; ++r) {
-    if (r * kThreads >= items) break;  // uniform; rounds with items keep whole waves (items % 64 == 0)
-    const int it = tid + r * kThreads;
-    const bool valid = it < items;
-    const int ms = it >> 4;
-    const int m = (int)(((float)ms + 0.5f) * inv_nsp);
-    const int sp = ms - m * nsp;
-    uint32_t wd[16];
-#pragma unroll
-    for (int d = 0; d < 16; ++d) wd[d] = L.q[r][d >> 2][d & 3];
-    uint32_t hi[4][2], lo[4][2];
-    int sc;
-    float X;
-    q1_convert_word(wd, hi, lo, sc, X);
-    // sum over the group's 4 words (neighbouring lanes)
-    X += dpp_xor1(X);
-    X += dpp_xor2(X);
-    if (valid) {
-      // A chunk (row, quarter qa = 2*(b & 1) + c, block (g4, b >> 1)) holds in
-      // dword 2*(j & 1) + hh the class-j bytes of half word hh, j >> 1 == c
-      unsigned char* base = lds + sp * Lay::kSpan;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int qa = 2 * (b & 1) + c;
-        *reinterpret_cast<u32x4*>(base + Lay::chunk(blk, qa, m)) =
-            u32x4{hi[2 * c][0], hi[2 * c][1], hi[2 * c + 1][0], hi[2 * c + 1][1]};
-        *reinterpret_cast<u32x4*>(base + Lay::chunk(blk, qa, 8 + m)) =
-            u32x4{lo[2 * c][0], lo[2 * c][1], lo[2 * c + 1][0], lo[2 * c + 1][1]};
-      }
-      base[Lay::kSc + (m + 16 * b) * 4 + g4] = (unsigned char)(sc + 127);
-      base[Lay::kSc + (8 + m + 16 * b) * 4 + g4] = (unsigned char)(sc + 123);
-      if (b == 0) reinterpret_cast<float*>(base + Lay::kXs)[g4 * 16 + m] = AFFINE ? X : -0.5f * X;
-    }
-  }
-}
-
-// Affine conversion (AffLay<RT>): three E5M2 pieces per activation.  Zeroes
-// A rows 12..15 and their scale bytes (1.0), and the group-sum entries no
-// live piece-0 lane owns; the rows of activation index >= M inside a row
-// tile are left unwritten (the MFMA keeps rows apart, and those results are
-// never read).
-template <int RT>
-__device__ void prep_compute_aff(const MmaArgs& a, int nsp, unsigned char* lds, int tid, const PrepLoads& L) {
-  using Lay = AffLay<RT>;
-  using AL = ALay<8>;
-  // zero rows 12..15: per span and row tile, 8 blocks x 4 quarters x 4 rows
-  for (int idx = tid; idx < nsp * RT * 128; idx += kThreads) {
-    const int c = idx & 127, srt = idx >> 7;
-    const int sp = srt / RT, rt = srt - sp * RT;
-    const int blk = c >> 4, qa = (c >> 2) & 3, r = 12 + (c & 3);
-    *reinterpret_cast<u32x4*>(lds + sp * Lay::kSpan + rt * Lay::kTileA + AL::chunk(blk, qa, r)) = u32x4{0u, 0u, 0u, 0u};
-  }
-  // their scale dwords (lanes 12..15 + 16 j) and the group-sum entries
-  // [g4][rt][16] that no conversion writes
-  for (int idx = tid; idx < nsp * RT * 16; idx += kThreads) {
-    const int j = idx & 3, r = 12 + ((idx >> 2) & 3), srt = idx >> 4;
-    const int sp = srt / RT, rt = srt - sp * RT;
-    reinterpret_cast<uint32_t*>(lds + sp * Lay::kSpan + Lay::kSc + rt * 256)[r + 16 * j] = 0x7f7f7f7fu;
-  }
-  for (int idx = tid; idx < nsp * 4 * RT * 16; idx += kThreads) {
-    const int e = idx & 15, rest = idx >> 4;  // rest = (sp * 4 + g4) * RT + rt
-    const int rt = rest % RT;
-    if (e >= 4 || 4 * rt + e >= a.M)
-      reinterpret_cast<float*>(lds + (rest / (4 * RT)) * Lay::kSpan + Lay::kXs)[(rest % (4 * RT)) * 16 + e] = 0.0f;
-  }
-  const int items = a.M * nsp * 16;
-  const int wi = tid & 15;
-  const int g4 = wi >> 2, b = wi & 3;
-  const int blk = 2 * g4 + (b >> 1);
-  const float inv_nsp = 1.0f / (float)nsp;
-#pragma unroll
-  for (int r = 0; r < kPrepRounds; ++r) {
-    if (r * kThreads >= items) break;  // uniform
-    const int it = tid + r * kThreads;
-    const bool valid = it < items;
-    const int ms = it >> 4;
-    const int m = (int)(((float)ms + 0.5f) * inv_nsp);
-    const int sp = ms - m * nsp;
-    uint32_t wd[16];
-#pragma unroll
-    for (int d = 0; d < 16; ++d) wd[d] = L.q[r][d >> 2][d & 3];
-    uint32_t pc[3][4][2];
-    int sc[3];
-    float X;
-    q1_convert_word_bf8(wd, pc, sc, X);
-    X += dpp_xor1(X);
-    X += dpp_xor2(X);
-    if (valid) {
-      const int rt = m >> 2, i = m & 3;
-      unsigned char* base = lds + sp * Lay::kSpan;
-#pragma unroll
-      for (int p = 0; p < 3; ++p) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int qa = 2 * (b & 1) + c;
-          *reinterpret_cast<u32x4*>(base + rt * Lay::kTileA + AL::chunk(blk, qa, 4 * p + i)) =
-              u32x4{pc[p][2 * c][0], pc[p][2 * c][1], pc[p][2 * c + 1][0], pc[p][2 * c + 1][1]};
-        }
-        base[Lay::kSc + rt * 256 + (4 * p + i + 16 * b) * 4 + g4] = (unsigned char)(sc[p] + 127);
-      }
-      if (b == 0) reinterpret_cast<float*>(base + Lay::kXs)[(g4 * RT + rt) * 16 + i] = X;
-    }
-  }
-}
-
-template <bool MBF16>
-__device__ __forceinline__ float meta_f32(uint32_t bits) {
-  return MBF16 ? __uint_as_float(bits << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-}
-
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
-// (lgkmcnt 0), not for its global loads, so the load ring stays in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
-  __builtin_amdgcn_s_barrier();
-}
-
-// 4x4 transpose of (lane quarter, component): afterwards quarter q holds, in
-// component c, what quarter c held in component q.
-__device__ __forceinline__ void transpose_quarters(u32x4& w) {
-  auto r02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
-  auto r13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
-  auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
-  auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
-  w[0] = r01[0];
-  w[1] = r01[1];
-  w[2] = r23[0];
-  w[3] = r23[1];
-}
-
-// Scales (or biases) of one row for the 8 groups of a double span, packed as
-// 16-bit values two per register.  With G % 8 == 0 they are one aligned
-// 16-byte load; otherwise 8 loads of 16 bits (groups past the end read 0).
-// (The 16-bit loads are combined only at use: combining them right after
-// issue would make the wave wait for them.)
-template <bool SC128>
-__device__ __forceinline__ void load_meta8(__amdgpu_buffer_rsrc_t r, bool rowok, uint32_t row_off, int G, int g0,
-                                           uint32_t* v) {
-  if (SC128) {
-    const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(r, (row_off + (uint32_t)g0 * 2) | (rowok ? 0u : kOOB), 0, kNTLoad);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = d[i];
-  } else {
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const uint32_t o = (row_off + (uint32_t)(g0 + g) * 2) | ((rowok && g0 + g < G) ? 0u : kOOB);
-      v[g] = __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, kNTLoad);
-    }
-  }
-}
-
-template <bool MBF16, bool SC128>
-__device__ __forceinline__ float meta_at(const uint32_t* v, int g) {
-  if (SC128) return meta_f32<MBF16>((g & 1) ? (v[g >> 1] >> 16) : (v[g >> 1] & 0xffffu));
-  return meta_f32<MBF16>(v[g]);
-}
-
-// One scaled MFMA for group g4 of a span (op_sel g4 picks the scale byte);
-// g4 is a constant after unrolling.  CBSZ: A format (0 fp8 E4M3, 1 bf8 E5M2);
-// B is fp4 (E2M1) with unit scales.
-template <int CBSZ>
-__device__ __forceinline__ v4f mfma_group(int g4, const v8i& A, const v8i& B, const v4f& C, uint32_t sa) {
-  switch (g4) {
-    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, CBSZ, 4, 0, (int)sa, 0, 0x7f7f7f7f);
-    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, CBSZ, 4, 1, (int)sa, 0, 0x7f7f7f7f);
-    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, CBSZ, 4, 2, (int)sa, 0, 0x7f7f7f7f);
-    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, CBSZ, 4, 3, (int)sa, 0, 0x7f7f7f7f);
-  }
-}
-
-// Work.  Workgroup p of K segment `seg` owns tiles p, p + P, p + 2P, .. (16
-// rows each; consecutive tiles go to different workgroups) and the segment's
-// double spans (8 groups, 128 bytes of every row).  Its items (local tile k,
-// double span d), tiles outer, are split evenly over its 8 waves: wave w takes
-// items [w*I/8, (w+1)*I/8).  Each wave leaves its sum for every tile its range
-// touches in LDS (slot = tile - its first tile); after the loop the slots of a
-// tile are added in wave order and stored.  The ring loop itself stores
-// nothing to memory: stores there would count in the same counter as the ring's
-// loads and make the waits for each slot's data also wait for newer loads.
-// Item i of a wave sits in ring slot i % D; its loads are issued D items
-// ahead.
-//
-// Loads: instruction h of an item reads rows 8h..8h+7 of the tile, lane l the
-// 16 bytes (group l%8, 4 words) of row l/8, so each row's 128 bytes come from
-// 8 neighbouring lanes.  The MFMA B operand wants lane (n, q) = word q of every
-// group of row n: the words go through a per-wave LDS scratch (row stride 34
-// dwords: the 8-byte writes and 4-byte reads are bank-conflict free).
-// MR: accumulator rows per lane quarter that can hold a live activation row
-// (1 for M = 1, 2 for M = 2, else 4); the others are never read, so their
-// scale multiply-adds are skipped.  RT (affine tensors): row tiles of 4
-// activation rows (1 for M <= 4, 2 for M = 5..8); symmetric tensors use one.
 template <bool AFFINE, bool MBF16, bool PAIR, bool SC128, int MR, int RT>
 __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
-  constexpr int RB = (AFFINE || MR == 4) ? 8 : MR;  // symmetric: A rows kept in LDS per half
-  using Lay = ALay<RB>;
-  constexpr int kSpanB = AFFINE ? AffLay<RT>::kSpan : Lay::kSpan;
-  constexpr int NMAT = PAIR ? 2 : 1;
-  // Ring slots (items in flight + those being computed).  Two: more items in
-  // flight per wave congest the memory pipeline the waves issue into
-  // (measured at K=5120, N=17408: 2 slots 2-5 % faster than 4 at M=2..8;
-  // at K=17408, N=5120 9 % at M=1, 2; 3, 5, 6 slots slower than 4 at M=4).
-  constexpr int D = 2;
-  constexpr int NSC = SC128 ? 4 : 8;  // registers of metadata per row and item
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int last_flag;
   __shared__ int wave_k0[kNW];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int seg = (int)(blockIdx.x % (unsigned)a.S);
-  const int p = (int)(blockIdx.x / (unsigned)a.S);
-  const int span0 = seg * a.KSP;                                    // even
-  const int nsp = (span0 + a.KSP <= a.nspan) ? a.KSP : a.nspan - span0;
-  const int nds = (nsp + 1) >> 1;                                   // double spans of the segment
-  const int ntiles = (int)((a.N + 15) >> 4);
-  const int nbp = (ntiles - p + a.P - 1) / a.P;                     // tiles of this workgroup
-  const int I = nbp * nds;                                          // items of this workgroup
-  const int i0 = (wave * I) / kNW, i1 = ((wave + 1) * I) / kNW;
-  const int nitems = i1 - i0;
-  // [w][slot][mt][ab][64] (affine: [w][slot][mt][rt][64])
-  float* red = reinterpret_cast<float*>(lds + (size_t)a.KSP * kSpanB);
-  uint32_t* scr = reinterpret_cast<uint32_t*>(lds + (size_t)a.KSP * kSpanB + (size_t)a.red_bytes) +
-                  wave * (NMAT * kScrDwords);
-
-  const __amdgpu_buffer_rsrc_t rp[2] = {rsrc(a.p0, a.packed_bytes), rsrc(PAIR ? a.p1 : a.p0, a.packed_bytes)};
-  const __amdgpu_buffer_rsrc_t rs[2] = {rsrc(a.s0, a.meta_bytes), rsrc(PAIR ? a.s1 : a.s0, a.meta_bytes)};
-  const __amdgpu_buffer_rsrc_t rbias[2] = {rsrc(AFFINE ? a.b0 : a.s0, a.meta_bytes),
-                                           rsrc(AFFINE && PAIR ? a.b1 : a.s0, a.meta_bytes)};
-
-  const int nl = lane & 15;   // weight row within a tile (B and D column)
-  const int q = lane >> 4;    // lane quarter
-  const int lr = lane >> 3;   // row within a load instruction
-  const int lc = lane & 7;    // 16-byte chunk (group) within a row's 128 bytes
-  const int a_lane0 = Lay::chunk(0, q, nl);  // (RB < 8) this lane's A chunk within a block
-  const uint32_t row_bytes = (uint32_t)a.K >> 3;
-  // row indices fit in 31 bits (the plan keeps N*K/8 below 2^31)
-  const int Nrows = (int)a.N;
-  auto tile_of = [&](int k) -> int { return k * a.P + p; };
-
-  u32x4 words[D][NMAT][2];
-  uint32_t sreg[D][NMAT][NSC];
-  uint32_t breg[D][NMAT][NSC];
-  float acc[NMAT][4 * RT];  // [mt][rt * 4 + i]
-#pragma unroll
-  for (int mt = 0; mt < NMAT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4 * RT; ++i) acc[mt][i] = 0.0f;
-
-  // issue the loads of item (local tile k, double span d) into slot u
-  auto issue = [&](int u, int k, int d, bool ok) {
-    const int sp = span0 + 2 * d;  // first span of the double span
-    const int r0 = tile_of(k) * 16 + lr;
-    const int g = 4 * sp + lc;     // this lane's group
-    const uint32_t col = (uint32_t)(sp * 64) + (uint32_t)lc * 16u;
-    const bool gok = ok && g < a.G;
-    const uint32_t o0 = ((uint32_t)r0 * row_bytes + col) | ((gok && r0 < Nrows) ? 0u : kOOB);
-    const uint32_t o1 = ((uint32_t)(r0 + 8) * row_bytes + col) | ((gok && r0 + 8 < Nrows) ? 0u : kOOB);
-    const int n = tile_of(k) * 16 + nl;
-    const bool nok = ok && n < Nrows;
-    const uint32_t mo = (uint32_t)n * (uint32_t)a.G * 2u;
-#pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) {
-      words[u][mt][0] = __builtin_amdgcn_raw_buffer_load_b128(rp[mt], o0, 0, kNTLoad);
-      words[u][mt][1] = __builtin_amdgcn_raw_buffer_load_b128(rp[mt], o1, 0, kNTLoad);
-      load_meta8<SC128>(rs[mt], nok, mo, a.G, 4 * sp, sreg[u][mt]);
-      if (AFFINE) load_meta8<SC128>(rbias[mt], nok, mo, a.G, 4 * sp, breg[u][mt]);
-    }
-  };
-
-  // activation loads first, then the first item of weights, the conversion
-  // (which waits for the activations only), then the other D - 1 items.  A
-  // wave issues its loads in order and stalls while the memory pipeline is
-  // full, so issuing all D items before the conversion delays it (measured:
-  // 5-7 % slower at config 2).  Slots are still issued in the loop's order,
-  // so the loop-head waits stay exact.
-  PrepLoads pl;
-  prep_load(a, span0, 2 * nds, tid, pl);
-  int pk = i0 / (nds > 0 ? nds : 1), pd = i0 - pk * nds;
-  auto issue_next = [&](int u) {
-    issue(u, pk, pd, u < nitems);
-    __builtin_amdgcn_sched_barrier(0);
-    if (++pd == nds) {
-      pd = 0;
-      ++pk;
-    }
-  };
-  issue_next(0);
-  if constexpr (AFFINE)
-    prep_compute_aff<RT>(a, 2 * nds, lds, tid, pl);
-  else
-    prep_compute<false, RB>(a, 2 * nds, lds, tid, pl);
-#pragma unroll
-  for (int u = 1; u < D; ++u) issue_next(u);
-  lds_barrier();
-
-  auto compute = [&](int u, int d) {
-    // B words of all groups: lane (n, q) gets word q of groups 0..7 of row n
-    uint32_t bw[NMAT][8];
-#pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) {
-      uint32_t* t = scr + mt * kScrDwords;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint2* dst = reinterpret_cast<uint2*>(t + (8 * h + lr) * kScrStride + 4 * lc);
-        dst[0] = uint2{words[u][mt][h][0], words[u][mt][h][1]};
-        dst[1] = uint2{words[u][mt][h][2], words[u][mt][h][3]};
-      }
-#pragma unroll
-      for (int g = 0; g < 8; ++g) bw[mt][g] = t[nl * kScrStride + 4 * g + q];
-    }
-    if constexpr (AFFINE) {
-      using AL = AffLay<RT>;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const unsigned char* base = lds + (2 * d + half) * kSpanB;
-        uint32_t scale_a[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          scale_a[rt] = reinterpret_cast<const uint32_t*>(base + AL::kSc + rt * 256)[lane];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          v8i A[RT];
-          v4f XS[RT];
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            const unsigned char* tb = base + rt * AL::kTileA;
-            const int lane_sw = lane ^ q;
-            const u32x4 h0 = reinterpret_cast<const u32x4*>(tb + a_blk_off(2 * g4))[lane_sw ^ ((g4 & 1) << 3)];
-            const u32x4 h1 = reinterpret_cast<const u32x4*>(tb + a_blk_off(2 * g4 + 1))[lane_sw ^ (4 | ((g4 & 1) << 3))];
-            A[rt] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-            XS[rt] = reinterpret_cast<const v4f*>(base + AL::kXs)[(g4 * RT + rt) * 4 + q];
-          }
-#pragma unroll
-          for (int mt = 0; mt < NMAT; ++mt) {
-            // weights of the two codes; the product runs over the code whose
-            // weight is larger in magnitude (d), the other enters through X
-            const float sv = meta_at<MBF16, SC128>(sreg[u][mt], 4 * half + g4);
-            const float bv = meta_at<MBF16, SC128>(breg[u][mt], 4 * half + g4);
-            const float w1 = sv + bv;
-            const bool d1 = fabsf(w1) >= fabsf(bv);
-            const float dw = w1 - bv;
-            const float sd = d1 ? dw : -dw;  // w_d - w_o
-            const float wo = d1 ? bv : w1;
-            const uint32_t wd = bw[mt][4 * half + g4] ^ (d1 ? 0u : 0xffffffffu);
-            const v8i B = {(int)(wd & 0x11111111u), (int)(wd & 0x22222222u), (int)(wd & 0x44444444u),
-                           (int)((wd >> 1) & 0x44444444u), 0, 0, 0, 0};
-            const v4f zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-              const v4f Dv = mfma_group<1>(g4, A[rt], B, zero, scale_a[rt]);
-#pragma unroll
-              for (int i = 0; i < MR; ++i) {
-                acc[mt][4 * rt + i] = fmaf(sd, Dv[i], acc[mt][4 * rt + i]);
-                acc[mt][4 * rt + i] = fmaf(wo, XS[rt][i], acc[mt][4 * rt + i]);
-              }
-            }
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const unsigned char* base = lds + (2 * d + half) * Lay::kSpan;
-        const uint32_t scale_a = reinterpret_cast<const uint32_t*>(base + Lay::kSc)[lane];
-        v8i A[4];
-        v4f XS[4];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          u32x4 h0, h1;
-          if (RB == 8) {
-            const int lane_sw = lane ^ q;  // position before the block's part of the swizzle
-            h0 = reinterpret_cast<const u32x4*>(base + a_blk_off(2 * g4))[lane_sw ^ ((g4 & 1) << 3)];
-            h1 = reinterpret_cast<const u32x4*>(base + a_blk_off(2 * g4 + 1))[lane_sw ^ (4 | ((g4 & 1) << 3))];
-          } else {
-            h0 = *reinterpret_cast<const u32x4*>(base + 2 * g4 * (128 * RB) + a_lane0);
-            h1 = *reinterpret_cast<const u32x4*>(base + (2 * g4 + 1) * (128 * RB) + a_lane0);
-          }
-          A[g4] = v8i{(int)h0[0], (int)h0[1], (int)h0[2], (int)h0[3], (int)h1[0], (int)h1[1], (int)h1[2], (int)h1[3]};
-          XS[g4] = reinterpret_cast<const v4f*>(base + Lay::kXs)[g4 * 4 + q];
-        }
-#pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt) {
-          v4f Dg[4];
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const uint32_t wd = bw[mt][4 * half + g4];
-            const v8i B = {(int)(wd & 0x11111111u), (int)(wd & 0x22222222u), (int)(wd & 0x44444444u),
-                           (int)((wd >> 1) & 0x44444444u), 0, 0, 0, 0};
-            Dg[g4] = mfma_group<0>(g4, A[g4], B, XS[g4], scale_a);  // C = -X/2
-          }
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const float sv = meta_at<MBF16, SC128>(sreg[u][mt], 4 * half + g4);
-#pragma unroll
-            for (int i = 0; i < MR; ++i) acc[mt][i] = fmaf(sv, Dg[g4][i], acc[mt][i]);
-          }
-        }
-      }
-    }
-  };
-
-  // one result (activation row m, weight row `row`): the output, or with a
-  // split K the segment's partial sum
-  auto emit = [&](int m, int row, const float* v) {
-    if (a.S == 1) {
-      if (PAIR)
-        static_cast<uint16_t*>(a.out)[m * a.out_ld + row] = (uint16_t)f32_to_bf16_bits(silu_f32(v[0]) * v[1]);
-      else
-        store_out(a.out, a.out_dtype, m * a.out_ld + row, v[0]);
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt)
-        __hip_atomic_store(&a.partial[(((int64_t)seg * a.M + m) * NMAT + mt) * a.N + row], v[mt], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-  };
-
-  // End of this wave's part of local tile k: lane l of half ab holds
-  // activation row 4*((l>>4)&1) + 2*ab + (l>>5) of weight row l & 15 (hi + lo
-  // combined); it goes to LDS slot (wave, k - first tile of the wave).
-  const int kfirst = i0 / (nds > 0 ? nds : 1);
-  // Affine: quarter q of row tile rt holds piece q of activation rows
-  // 4 rt + i (element i); the four quarters are added (quarter 3 is zero),
-  // leaving activation row 4 rt + i in 16-lane row ((i & 1) << 1) | (i >> 1)
-  // of slot rt.
-  auto tile_done = [&](int k) {
-#pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) {
-      float* slot = red + (((wave * a.TW + (k - kfirst)) * NMAT + mt) * 2) * 64 + lane;
-      if constexpr (AFFINE) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const float* v = &acc[mt][4 * rt];
-          auto p01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[1]), false, false);
-          auto p23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[2]), __float_as_uint(v[3]), false, false);
-          const float s01 = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
-          const float s23 = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
-          auto pp = __builtin_amdgcn_permlane16_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
-          slot[64 * rt] = __uint_as_float(pp[0]) + __uint_as_float(pp[1]);
-        }
-      } else {
-        auto p01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[mt][0]), __float_as_uint(acc[mt][1]), false,
-                                                    false);
-        auto p23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[mt][2]), __float_as_uint(acc[mt][3]), false,
-                                                    false);
-        slot[0] = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
-        slot[64] = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4 * RT; ++i) acc[mt][i] = 0.0f;
-    }
-  };
-
-  // Whole turns of the ring (slots past the end load nothing, compute
-  // nothing and end no tile): a loop body without early exits keeps the ring
-  // in place across iterations.
-  const int nitems_pad = (nitems + D - 1) / D * D;
-  int k = kfirst, d = i0 - kfirst * nds;  // current item
-  int ik = k, id = d + D;                 // item + D (next loads)
-  while (nds > 0 && id >= nds) {
-    id -= nds;
-    ++ik;
-  }
-  for (int base = 0; base < nitems_pad; base += D) {
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-      if (base + u < nitems) compute(u, d);  // (uniform) the last turn's empty slots do no work
-      issue(u, ik, id, base + u + D < nitems);
-      __builtin_amdgcn_sched_barrier(0);  // keep items apart: bounded register use
-      if (base + u < nitems && (d == nds - 1 || base + u == nitems - 1)) tile_done(k);
-      if (++d == nds) {
-        d = 0;
-        ++k;
-      }
-      if (++id == nds) {
-        id = 0;
-        ++ik;
-      }
-    }
-  }
-
-  // ---- tile results: the slots of the waves that touched each tile, in
-  // wave order.  Thread o takes (tile kk, activation row m, weight row r),
-  // rows fastest; the waves' first tiles come through LDS, so the loop does
-  // no integer division. ----
-  if (lane == 0) wave_k0[wave] = kfirst;
-  lds_barrier();
-  {
-    const int per_t = 16 * a.M;
-    const float inv_per_t = 1.0f / (float)per_t;
-    const float inv_I = I > 0 ? 1.0f / (float)I : 0.0f;
-    for (int o = tid; o < nbp * per_t; o += kThreads) {
-      const int kk = (int)(((float)o + 0.5f) * inv_per_t);  // o / per_t (exact: o < 2^22)
-      const int rem = o - kk * per_t;
-      const int m = rem >> 4, r = rem & 15;
-      const int row = tile_of(kk) * 16 + r;
-      if (row >= Nrows) continue;
-      const int t0 = kk * nds, t1 = t0 + nds;  // the tile's items
-      // wave holding item t0: the last w with w*I/8 <= t0 (estimate, then exact)
-      int wa = (int)((float)(8 * t0 + 7) * inv_I);
-      wa = wa > kNW - 1 ? kNW - 1 : wa;
-      while (wa > 0 && ((wa * I) >> 3) > t0) --wa;
-      while (wa < kNW - 1 && (((wa + 1) * I) >> 3) <= t0) ++wa;
-      // position of (m, r) in the slots (see tile_done)
-      const int l = AFFINE ? r + 16 * (((m & 1) << 1) | ((m >> 1) & 1)) : r + 16 * ((m >> 2) & 1) + 32 * (m & 1);
-      const int ab = AFFINE ? (m >> 2) : (m >> 1) & 1;
-      float v[NMAT];
-#pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt) v[mt] = 0.0f;
-      for (int w2 = wa; w2 < kNW && ((w2 * I) >> 3) < t1; ++w2) {
-        if ((((w2 + 1) * I) >> 3) == ((w2 * I) >> 3)) continue;  // wave without items
-        const int sl = kk - wave_k0[w2];
-#pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt) v[mt] += red[(((w2 * a.TW + sl) * NMAT + mt) * 2 + ab) * 64 + l];
-      }
-      emit(m, row, v);
-    }
-  }
-  if (a.S == 1) return;
-
-  // ---- split K: the last of the S workgroups with this p adds the
-  // partials of p's tiles in segment order.  The workgroup's partial stores
-  // happen before its arrival: a workgroup barrier, then an agent-scope
-  // release on the counter.  The last arrival's read of the counter is
-  // followed by one agent-scope acquire fence (thread 0), and the barrier
-  // that hands out the flag orders the other waves' reads after it.  (An
-  // acquire in every wave costs an L2 invalidation each: measured +8 us at
-  // K=17408, N=5120, against +1 us for the single one; acq_rel on every
-  // arrival +2 us.) ----
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&a.counters[p], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = old == (uint32_t)(a.S - 1);
-    if (last_flag) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  const int per_m = nbp * 16;
-  const float inv_per_m = 1.0f / (float)per_m;
-  for (int o = tid; o < per_m * a.M; o += kThreads) {
-    const int m = (int)(((float)o + 0.5f) * inv_per_m);  // o / per_m (exact: o < 2^22)
-    const int rem = o - m * per_m;
-    const int row = tile_of(rem >> 4) * 16 + (rem & 15);
-    if (row >= Nrows) continue;
-    float v[NMAT];
-#pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) {
-      float sum = 0.0f;
-      for (int s2 = 0; s2 < a.S; ++s2)
-        sum += __hip_atomic_load(&a.partial[(((int64_t)s2 * a.M + m) * NMAT + mt) * a.N + row], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-      v[mt] = sum;
-    }
-    if (PAIR)
-      static_cast<uint16_t*>(a.out)[m * a.out_ld + row] = (uint16_t)f32_to_bf16_bits(silu_f32(v[0]) * v[1]);
-    else
-      store_out(a.out, a.out_dtype, m * a.out_ld + row, v[0]);
-  }
-  if (tid == 0) __hip_atomic_store(&a.counters[p], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  mma_stage<AFFINE, MBF16, PAIR, SC128, MR, RT>(a, (int)(blockIdx.x % (unsigned)a.S), (int)(blockIdx.x / (unsigned)a.S),
+                                                lds, &last_flag, wave_k0, NoWait{});
 }
 
 template <bool AFFINE, bool MBF16, bool PAIR, bool SC128, int MR, int RT>
@@ -807,6 +59,38 @@ hipError_t launch_t(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
 
 }  // namespace
 
+bool plan_mma_split(int M, int64_t N, int64_t K, bool pair, bool affine, int S, int64_t P, MmaPlan* c) {
+  const int nmat = pair ? 2 : 1;
+  c->M = M;
+  c->pair = pair ? 1 : 0;
+  c->G = (int)(K / 128);
+  c->nspan = (c->G + 3) / 4;
+  c->ntiles = (N + 15) / 16;
+  const int ndsp = (c->nspan + 1) / 2;  // double spans
+  if (S < 1 || S > ndsp || P < 1) return false;
+  const int kds = (ndsp + S - 1) / S;
+  c->S = (ndsp + kds - 1) / kds;
+  if (c->S != S) return false;  // same split as a smaller S
+  c->KSP = 2 * kds;
+  c->P = (int)std::min<int64_t>(P, c->ntiles);
+  c->nb = (int)((c->ntiles + c->P - 1) / c->P);  // tiles per workgroup (at most)
+  c->wgs = (int64_t)c->S * c->P;
+  // Tiles one wave's item range [i0, i1) touches: floor((i1-1)/nds) -
+  // floor(i0/nds) + 1 < (i1-1-i0)/nds + 2 < nbp/8 + 2 for every workgroup
+  // size nbp <= nb and segment length nds, so at most ceil(nb/8) + 1.
+  c->TW = (int)std::min<int64_t>(c->nb, (c->nb + kNW - 1) / kNW + 1);
+  const int rb = (pair || M > 2) ? 8 : M;
+  const size_t span = affine ? (size_t)aff_span_bytes(M > 4 ? 2 : 1) : (size_t)span_bytes(rb);
+  const size_t scratch = (size_t)kNW * nmat * kScrDwords * 4;
+  c->red_bytes = (size_t)kNW * c->TW * nmat * 512;
+  c->lds_bytes = (size_t)c->KSP * span + c->red_bytes + scratch;
+  if (c->lds_bytes > 160 * 1024 - 64 || (int64_t)M * c->KSP * 16 > (int64_t)kPrepRounds * kThreads) return false;
+  if ((int64_t)c->nb * 128 >= ((int64_t)1 << 22)) return false;  // result-slot index arithmetic
+  c->partial_floats = c->S > 1 ? (size_t)c->S * M * N * nmat : 0;
+  c->counters = c->S > 1 ? (size_t)c->P : 0;  // one per workgroup column p (P <= CUs)
+  return true;
+}
+
 bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, const char** why) {
   if (M < 1 || M > 8) {
     *why = "matrix-core packed path handles 1..8 activation rows";
@@ -821,18 +105,8 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, c
     *why = "matrix too large for 32-bit buffer offsets (split it along N)";
     return false;
   }
-  const int nmat = pair ? 2 : 1;
   const int cus = device_cus();
-  p->M = M;
-  p->pair = pair ? 1 : 0;
-  p->G = (int)(K / 128);
-  p->nspan = (p->G + 3) / 4;
-  p->ntiles = (N + 15) / 16;
-  const int ndsp = (p->nspan + 1) / 2;  // double spans
-  const int rb = (pair || M > 2) ? 8 : M;
-  const size_t span = affine ? (size_t)aff_span_bytes(M > 4 ? 2 : 1) : (size_t)span_bytes(rb);
-  const size_t scratch = (size_t)kNW * nmat * kScrDwords * 4;
-  const size_t budget = 160 * 1024 - 64;
+  const int ndsp = ((int)(K / 128) + 7) / 8;
   // Number of K segments S: among the splits whose LDS image, result slots
   // and scratch fit, the one with the fewest items in the busiest workgroup
   // (tiles are whole per workgroup, so S also balances the work), where a
@@ -841,25 +115,9 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, c
   MmaPlan best;
   int64_t best_cost = -1;
   for (int S = 1; S <= ndsp; ++S) {
-    MmaPlan c = *p;
-    const int kds = (ndsp + S - 1) / S;
-    c.S = (ndsp + kds - 1) / kds;
-    if (c.S != S) continue;  // same split as a smaller S
-    c.KSP = 2 * kds;
-    int64_t P = c.ntiles;
-    const int64_t cap = cus / c.S > 0 ? cus / c.S : 1;
-    if (P > cap) P = cap;
-    c.P = (int)P;
-    c.nb = (int)((c.ntiles + P - 1) / P);  // tiles per workgroup (at most)
-    c.wgs = (int64_t)c.S * P;
-    // Tiles one wave's item range [i0, i1) touches: floor((i1-1)/nds) -
-    // floor(i0/nds) + 1 < (i1-1-i0)/nds + 2 < nbp/8 + 2 for every workgroup
-    // size nbp <= nb and segment length nds, so at most ceil(nb/8) + 1.
-    c.TW = (int)std::min<int64_t>(c.nb, (c.nb + kNW - 1) / kNW + 1);
-    c.red_bytes = (size_t)kNW * c.TW * nmat * 512;
-    c.lds_bytes = (size_t)c.KSP * span + c.red_bytes + scratch;
-    if (c.lds_bytes > budget || (int64_t)M * c.KSP * 16 > (int64_t)kPrepRounds * kThreads) continue;
-    const int64_t cost = (int64_t)c.nb * kds + (c.S > 1 ? 6 + c.S / 2 : 0);
+    MmaPlan c;
+    if (!plan_mma_split(M, N, K, pair, affine, S, cus / S > 0 ? cus / S : 1, &c)) continue;
+    const int64_t cost = (int64_t)c.nb * (c.KSP / 2) + (c.S > 1 ? 6 + c.S / 2 : 0);
     if (best_cost < 0 || cost < best_cost) {
       best = c;
       best_cost = cost;
@@ -870,17 +128,11 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, c
     return false;
   }
   *p = best;
-  if ((int64_t)p->nb * 128 >= ((int64_t)1 << 22)) {
-    *why = "too many tiles per workgroup for the result slots";
-    return false;
-  }
-  p->partial_floats = p->S > 1 ? (size_t)p->S * M * N * nmat : 0;
-  p->counters = p->S > 1 ? (size_t)p->P : 0;  // one per workgroup column p (P <= CUs)
   return true;
 }
 
-hipError_t launch_mma(const MmaPlan& p, const uint16_t* x, int64_t x_ld, const QMat& a, const QMat* b, void* out,
-                      int32_t out_dtype, int64_t out_ld, float* partial, uint32_t* counters, hipStream_t s) {
+MmaArgs mma_args(const MmaPlan& p, const uint16_t* x, int64_t x_ld, const QMat& a, const QMat* b, void* out,
+                 int32_t out_dtype, int64_t out_ld, float* partial, uint32_t* counters) {
   MmaArgs g;
   g.x = x;
   g.x_ld = x_ld;
@@ -909,6 +161,12 @@ hipError_t launch_mma(const MmaPlan& p, const uint16_t* x, int64_t x_ld, const Q
   g.out_ld = out_ld;
   g.partial = partial;
   g.counters = counters;
+  return g;
+}
+
+hipError_t launch_mma(const MmaPlan& p, const uint16_t* x, int64_t x_ld, const QMat& a, const QMat* b, void* out,
+                      int32_t out_dtype, int64_t out_ld, float* partial, uint32_t* counters, hipStream_t s) {
+  const MmaArgs g = mma_args(p, x, x_ld, a, b, out, out_dtype, out_ld, partial, counters);
   const bool affine = !a.symmetric, mbf16 = a.meta_bf16 != 0, pair = b != nullptr;
   if (pair) {
     if (affine) return mbf16 ? launch_t<true, true, true>(p, g, s) : launch_t<true, false, true>(p, g, s);

@@ -53,8 +53,12 @@ typedef enum q1_dtype { Q1_F32 = 0, Q1_F16 = 1, Q1_BF16 = 2 } q1_dtype;
 /* The first Q1_WS_RESERVED_BYTES bytes of every workspace hold split-K
  * arrival counters.  They must be zero before a workspace is first used; every
  * call leaves them zero again once the stream has executed it, and no call
- * writes anything else there.  All other temporaries start after them. */
+ * writes anything else there, with one exception: the single-launch q1_ffn
+ * sets the last uint32 of the block (Q1_WS_STATUS_WORD, an index in uint32
+ * units) to 1 if one of its waits gives up (see q1_ffn); nothing clears it but
+ * the caller.  All other temporaries start after the block. */
 #define Q1_WS_RESERVED_BYTES 16384
+#define Q1_WS_STATUS_WORD (Q1_WS_RESERVED_BYTES / 4 - 1)
 
 /* One packed Q1 matrix (caller-owned device memory). */
 typedef struct q1_weight {
@@ -144,7 +148,18 @@ q1_status q1_embed_rows(const void* ids, int32_t ids_are_int64, int64_t T, const
  *   y      bf16 [M, H_out]
  *   Gate and up accumulate in fp32; h = SiLU(g)*u is rounded once to bf16 and
  *   is left in the workspace at byte offset Q1_WS_RESERVED_BYTES (bf16 [M, I]).
- *   M <= max packed rows: gate+up in one packed launch with the SiLU*mul
+ *   With Q1_FFN_KERNEL=single (read on every call and by the workspace
+ *   query), M <= max packed rows, all three matrices of one kind (symmetry
+ *   and metadata dtype) and H, I multiples of 1024: ONE launch, one
+ *   workgroup per compute unit.  Its workgroups first compute gate/up tiles and their h
+ *   rows, then each takes a K segment of the down projection and waits until
+ *   every h row of that segment is written.  The waits end because the whole
+ *   grid is resident; should one still spin past its bound (about a second;
+ *   only another kernel holding compute units that long can cause it), the
+ *   launch sets workspace uint32 Q1_WS_STATUS_WORD to 1, finishes with y
+ *   undefined, and still leaves the other counters zero.  (On MI355X it is
+ *   slower than the default below.)  Otherwise, for M <= max packed
+ *   rows: gate+up in one packed launch with the SiLU*mul
  *   epilogue (when gate and up share metadata dtype and symmetry; otherwise
  *   two packed launches and an element-wise kernel), then the packed down
  *   projection.  M > max packed rows: the wide path of q1_qmm per projection
