@@ -478,10 +478,20 @@ __device__ __forceinline__ void mma_stage(const MmaArgs& a, int seg, int p, unsi
     float v[NMAT];
 #pragma unroll
     for (int mt = 0; mt < NMAT; ++mt) {
+      // segment order; the loads go out four at a time (one after the other,
+      // each waited for before the next, they cost S memory latencies)
+      const float* pp = a.partial + ((int64_t)m * NMAT + mt) * a.N + row;
+      const int64_t sstep = (int64_t)a.M * NMAT * a.N;
+      auto ld = [&](int s2) { return __hip_atomic_load(pp + s2 * sstep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
       float sum = 0.0f;
-      for (int s2 = 0; s2 < a.S; ++s2)
-        sum += __hip_atomic_load(&a.partial[(((int64_t)s2 * a.M + m) * NMAT + mt) * a.N + row], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+      for (int s2 = 0; s2 < a.S; s2 += 4) {  // a short last batch re-reads segment S-1 and drops it
+        const int sl = a.S - 1;
+        const float p0 = ld(s2), p1 = ld(min(s2 + 1, sl)), p2 = ld(min(s2 + 2, sl)), p3 = ld(min(s2 + 3, sl));
+        sum += p0;
+        if (s2 + 1 < a.S) sum += p1;
+        if (s2 + 2 < a.S) sum += p2;
+        if (s2 + 3 < a.S) sum += p3;
+      }
       v[mt] = sum;
     }
     if (PAIR)
