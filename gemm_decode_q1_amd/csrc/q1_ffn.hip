@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void q1_ffn_kernel(FfnArgs f) {
       }
       __syncthreads();
     };
-    mma_stage<AFFINE, MBF16, false, true, MR2, RT, true>(f.d, seg, p2, lds, &last_flag, wave_k0, wait_h);
+    mma_stage<AFFINE, MBF16, false, true, MR2, RT, true, true>(f.d, seg, p2, lds, &last_flag, wave_k0, wait_h);
   }
 
   __syncthreads();

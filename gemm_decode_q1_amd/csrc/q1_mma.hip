@@ -20,6 +20,40 @@ __global__ __launch_bounds__(kThreads) void q1_mma_kernel(MmaArgs a) {
                                                 lds, &last_flag, wave_k0, NoWait{});
 }
 
+// Split K: the S segments' partial sums [S][M][NMAT][N], added in segment
+// order (the stream runs this after the matmul launch); pair mode writes
+// h = bf16(SiLU(g) * u).  The loads go out four at a time.
+template <bool PAIR>
+__global__ __launch_bounds__(256) void q1_mma_reduce(const float* __restrict__ partial, int S, int M, int64_t N,
+                                                     void* out, int32_t out_dtype, int64_t out_ld) {
+  constexpr int NMAT = PAIR ? 2 : 1;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)M * N) return;
+  const int m = (int)(i / N);
+  const int64_t n = i - (int64_t)m * N;
+  const int64_t sstep = (int64_t)M * NMAT * N;
+  float v[NMAT];
+#pragma unroll
+  for (int mt = 0; mt < NMAT; ++mt) {
+    const float* pp = partial + ((int64_t)m * NMAT + mt) * N + n;
+    float sum = 0.0f;
+    for (int s2 = 0; s2 < S; s2 += 4) {  // a short last batch re-reads segment S-1 and drops it
+      const int sl = S - 1;
+      const float p0 = pp[s2 * sstep], p1 = pp[min(s2 + 1, sl) * sstep], p2 = pp[min(s2 + 2, sl) * sstep],
+                  p3 = pp[min(s2 + 3, sl) * sstep];
+      sum += p0;
+      if (s2 + 1 < S) sum += p1;
+      if (s2 + 2 < S) sum += p2;
+      if (s2 + 3 < S) sum += p3;
+    }
+    v[mt] = sum;
+  }
+  if (PAIR)
+    static_cast<uint16_t*>(out)[m * out_ld + n] = (uint16_t)f32_to_bf16_bits(silu_f32(v[0]) * v[1]);
+  else
+    store_out(out, out_dtype, m * out_ld + n, v[0]);
+}
+
 template <bool AFFINE, bool MBF16, bool PAIR, bool SC128, int MR, int RT>
 hipError_t launch_k(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
   static const hipError_t attr =
@@ -28,6 +62,11 @@ hipError_t launch_k(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((q1_mma_kernel<AFFINE, MBF16, PAIR, SC128, MR, RT>), dim3((unsigned)p.wgs), dim3(kThreads),
                      p.lds_bytes, s, a);
+  if (a.S > 1) {
+    const int64_t n = (int64_t)a.M * a.N;
+    hipLaunchKernelGGL((q1_mma_reduce<PAIR>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.partial, a.S, a.M,
+                       a.N, a.out, a.out_dtype, a.out_ld);
+  }
   return hipGetLastError();
 }
 
@@ -87,7 +126,7 @@ bool plan_mma_split(int M, int64_t N, int64_t K, bool pair, bool affine, int S, 
   if (c->lds_bytes > 160 * 1024 - 64 || (int64_t)M * c->KSP * 16 > (int64_t)kPrepRounds * kThreads) return false;
   if ((int64_t)c->nb * 128 >= ((int64_t)1 << 22)) return false;  // result-slot index arithmetic
   c->partial_floats = c->S > 1 ? (size_t)c->S * M * N * nmat : 0;
-  c->counters = c->S > 1 ? (size_t)c->P : 0;  // one per workgroup column p (P <= CUs)
+  c->counters = c->S > 1 ? (size_t)c->P : 0;  // per column p (P <= CUs); only the in-kernel handoff counts
   return true;
 }
 

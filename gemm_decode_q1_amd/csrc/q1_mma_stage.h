@@ -109,13 +109,19 @@ constexpr int kThreads = kNW * 64;
 // phase of the single-launch FFN (q1_ffn.hip).  WFIRST: issue the ring's first
 // weight loads, then call wait() (which returns once the activations are
 // readable), then load and convert the activations; otherwise the activation
-// loads go first (they gate the first MFMA).  A workgroup-uniform return ends
-// the stage; lds, last_flag and wave_k0 are the caller's LDS.
+// loads go first (they gate the first MFMA).  HANDOFF: with a split K, the
+// last of a column's S workgroups adds the segments' partial sums itself
+// (the single launch, which cannot launch again); otherwise the stage ends
+// with its partials stored and a second launch adds them (q1_mma_reduce:
+// the kernel boundary orders them, and measured 0.7-1.4 us faster than the
+// in-kernel handoff at K=17408, N=5120).  A workgroup-uniform return ends the
+// stage; lds, last_flag and wave_k0 are the caller's LDS.
 struct NoWait {
   __device__ __forceinline__ void operator()() const {}
 };
 
-template <bool AFFINE, bool MBF16, bool PAIR, bool SC128, int MR, int RT, bool WFIRST = false, class Wait = NoWait>
+template <bool AFFINE, bool MBF16, bool PAIR, bool SC128, int MR, int RT, bool WFIRST = false, bool HANDOFF = false,
+          class Wait = NoWait>
 __device__ __forceinline__ void mma_stage(const MmaArgs& a, int seg, int p, unsigned char* lds, int* last_flag_p,
                                           int* wave_k0, const Wait& wait) {
   constexpr int RB = (AFFINE || MR == 4) ? 8 : MR;  // symmetric: A rows kept in LDS per half
@@ -341,9 +347,13 @@ __device__ __forceinline__ void mma_stage(const MmaArgs& a, int seg, int p, unsi
         store_out(a.out, a.out_dtype, m * a.out_ld + row, v[0]);
     } else {
 #pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt)
-        __hip_atomic_store(&a.partial[(((int64_t)seg * a.M + m) * NMAT + mt) * a.N + row], v[mt], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      for (int mt = 0; mt < NMAT; ++mt) {
+        float* dst = &a.partial[(((int64_t)seg * a.M + m) * NMAT + mt) * a.N + row];
+        if (HANDOFF)
+          __hip_atomic_store(dst, v[mt], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          *dst = v[mt];
+      }
     }
   };
 
@@ -448,7 +458,7 @@ __device__ __forceinline__ void mma_stage(const MmaArgs& a, int seg, int p, unsi
       emit(m, row, v);
     }
   }
-  if (a.S == 1) return;
+  if (a.S == 1 || !HANDOFF) return;
 
   // ---- split K: the last of the S workgroups with this p adds the
   // partials of p's tiles in segment order.  The workgroup's partial stores
