@@ -103,7 +103,7 @@ struct MmaPlan {
   int G;           // groups of 128 along K
   int nspan;       // spans of 4 groups (512 weights)
   int64_t ntiles;  // tiles of 16 rows
-  int S;           // K segments (grid split); S > 1 finishes in the kernel
+  int S;           // K segments (grid split); S > 1: a reduce launch adds them
   int KSP;         // spans per K segment (the last may have fewer)
   int P;           // workgroups per K segment
   int nb;          // tiles per workgroup (at most)

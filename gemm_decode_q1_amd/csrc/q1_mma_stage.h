@@ -58,17 +58,16 @@
 //             32*(l/16) + e, so lane l/16 = q carries word q of the group.
 //   D lane l: column l%16, rows 4*(l/16) .. +3.
 //
-// Work decomposition.  A workgroup (8 waves) owns a block of row tiles (16
-// rows each) and a segment of K (spans of 4 groups).  First every thread
-// converts the segment's activations into the A operand image in LDS; then
-// wave (ws, wt) takes spans ws, ws+NWS.. of the segment and tiles wt, wt+NWT..
-// of the block.  A lane loads 16 bytes = one group's 4 words of one row; a
-// 4x4 transpose across the lane quarters (two permlane32 and two permlane16
-// swaps) gives lane quarter q word q of each of the 4 groups.  The waves'
-// partial sums meet in LDS and are added in a fixed order.  With more than one
-// K segment (grid split), each segment writes fp32 partials with agent-scope
-// stores and the last workgroup to finish a row block adds them in segment
-// order, so results never depend on timing.
+// Work decomposition.  A workgroup (8 waves) owns tiles of 16 weight rows and
+// a segment of K (spans of 4 groups).  First its threads convert the segment's
+// activations into the A operand image in LDS; then its items (tile, double
+// span) are split evenly over the waves, each lane loading 16 bytes (one
+// group's 4 words of one row) and a per-wave LDS transpose giving lane (n, q)
+// word q of each group of row n.  The waves' partial sums meet in LDS and are
+// added in a fixed order.  With more than one K segment (grid split), each
+// segment writes fp32 partials and a second launch adds them in segment order
+// (in the single-launch FFN, the last workgroup of a column does), so results
+// never depend on timing.
 #pragma once
 
 #include <hip/hip_runtime.h>
