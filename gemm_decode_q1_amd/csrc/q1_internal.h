@@ -113,6 +113,7 @@ struct MmaPlan {
   size_t lds_bytes;
   size_t partial_floats;  // S > 1: S*M*N*(pair ? 2 : 1)
   size_t counters;        // S > 1: P
+  int rb;                 // A rows per half in the LDS image: 8, or M (1, 2) for the compact image
 };
 
 struct MmaArgs {
@@ -140,7 +141,9 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* plan
 // The plan for a given split: S K segments of P workgroups each (P is
 // capped at the tile count).  False when S is not a distinct split of K or
 // the segment's LDS image, result slots and scratch do not fit.
-bool plan_mma_split(int M, int64_t N, int64_t K, bool pair, bool affine, int S, int64_t P, MmaPlan* plan);
+// full_image: keep all 8 A rows per half in the LDS image even for M <= 2.
+bool plan_mma_split(int M, int64_t N, int64_t K, bool pair, bool affine, int S, int64_t P, MmaPlan* plan,
+                    bool full_image = false);
 
 // Kernel arguments of one matrix-core stage (plan + operands).
 MmaArgs mma_args(const MmaPlan& plan, const uint16_t* x, int64_t x_ld, const QMat& a, const QMat* b, void* out,

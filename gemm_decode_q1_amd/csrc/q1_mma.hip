@@ -85,7 +85,8 @@ hipError_t launch_r(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
   } else if constexpr (PAIR) {
     return launch_k<AFFINE, MBF16, PAIR, SC128, 4, 1>(p, a, s);
   } else {
-    if (a.M > 2) return launch_k<AFFINE, MBF16, PAIR, SC128, 4, 1>(p, a, s);
+    // (the full image is the four-row layout: its extra rows are never read)
+    if (a.M > 2 || p.rb == 8) return launch_k<AFFINE, MBF16, PAIR, SC128, 4, 1>(p, a, s);
     return a.M == 1 ? launch_k<AFFINE, MBF16, PAIR, SC128, 1, 1>(p, a, s)
                     : launch_k<AFFINE, MBF16, PAIR, SC128, 2, 1>(p, a, s);
   }
@@ -98,7 +99,8 @@ hipError_t launch_t(const MmaPlan& p, const MmaArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool plan_mma_split(int M, int64_t N, int64_t K, bool pair, bool affine, int S, int64_t P, MmaPlan* c) {
+bool plan_mma_split(int M, int64_t N, int64_t K, bool pair, bool affine, int S, int64_t P, MmaPlan* c,
+                    bool full_image) {
   const int nmat = pair ? 2 : 1;
   c->M = M;
   c->pair = pair ? 1 : 0;
@@ -118,7 +120,8 @@ bool plan_mma_split(int M, int64_t N, int64_t K, bool pair, bool affine, int S, 
   // floor(i0/nds) + 1 < (i1-1-i0)/nds + 2 < nbp/8 + 2 for every workgroup
   // size nbp <= nb and segment length nds, so at most ceil(nb/8) + 1.
   c->TW = (int)std::min<int64_t>(c->nb, (c->nb + kNW - 1) / kNW + 1);
-  const int rb = (pair || M > 2) ? 8 : M;
+  const int rb = (pair || M > 2 || full_image) ? 8 : M;
+  c->rb = affine ? 8 : rb;
   const size_t span = affine ? (size_t)aff_span_bytes(M > 4 ? 2 : 1) : (size_t)span_bytes(rb);
   const size_t scratch = (size_t)kNW * nmat * kScrDwords * 4;
   c->red_bytes = (size_t)kNW * c->TW * nmat * 512;
@@ -151,15 +154,21 @@ bool plan_mma(int M, int64_t N, int64_t K, bool pair, bool affine, MmaPlan* p, c
   // (tiles are whole per workgroup, so S also balances the work), where a
   // split (the partial sums' round trips at the end, S partials per result)
   // counts as 6 + S/2 items (measured on the shapes with 17408-weight rows).
+  // With two activation rows the compact image (live A rows only) holds
+  // longer K segments, the full one is faster per item (K=5120, N=17408:
+  // 7.8 -> 7.4 us): the full image wins ties.
   MmaPlan best;
   int64_t best_cost = -1;
-  for (int S = 1; S <= ndsp; ++S) {
-    MmaPlan c;
-    if (!plan_mma_split(M, N, K, pair, affine, S, cus / S > 0 ? cus / S : 1, &c)) continue;
-    const int64_t cost = (int64_t)c.nb * (c.KSP / 2) + (c.S > 1 ? 6 + c.S / 2 : 0);
-    if (best_cost < 0 || cost < best_cost) {
-      best = c;
-      best_cost = cost;
+  const int layouts = (M == 2 && !pair && !affine) ? 2 : 1;
+  for (int full = layouts - 1; full >= 0; --full) {
+    for (int S = 1; S <= ndsp; ++S) {
+      MmaPlan c;
+      if (!plan_mma_split(M, N, K, pair, affine, S, cus / S > 0 ? cus / S : 1, &c, full != 0)) continue;
+      const int64_t cost = (int64_t)c.nb * (c.KSP / 2) + (c.S > 1 ? 6 + c.S / 2 : 0);
+      if (best_cost < 0 || cost < best_cost) {
+        best = c;
+        best_cost = cost;
+      }
     }
   }
   if (best_cost < 0) {
