@@ -112,9 +112,9 @@ q1_status hip_status(hipError_t e, const char* what) {
 
 // ---- workspace layouts --------------------------------------------------
 
-// Every workspace starts with Q1_WS_RESERVED_BYTES of arrival counters
-// (shared by all packed launches of a call, which run in stream order and each
-// leave them zero); a packed launch's fp32 partial sums go at `base`.
+// Every workspace starts with Q1_WS_RESERVED_BYTES reserved for the
+// single-launch FFN's counters and status word (the other launches leave it
+// untouched); a packed launch's fp32 partial sums go at `base`.
 constexpr size_t kReserved = Q1_WS_RESERVED_BYTES;
 
 // Packed narrow-M launches: the nibble-table kernel (q1_gemv.inc) for one
@@ -204,7 +204,7 @@ struct FfnWs {
   q1::FfnPlan fp;
   size_t part_off;                 // single: down split-K partials
   PackedPlan pgu, pg, pu, pd;
-  size_t h_off, gu_off, d_off;     // packed: counters+partials blocks
+  size_t h_off, gu_off, d_off;     // packed: partial-sum blocks
   size_t g_off, u_off;             // unfused / wide: fp32 g and u
   size_t deq_off;                  // wide: operand image (matrix-core path) or dequantised matrix
   bool wide_mma;                   // wide: matrix-core path
@@ -281,11 +281,10 @@ q1_status run_packed(const PackedPlan& p, const uint16_t* x, int64_t x_ld, const
   PackedWs w = packed_ws(p, base);
   const bool split = p.partial_floats() > 0;
   float* partial = split ? reinterpret_cast<float*>(ws + w.partial_off) : nullptr;
-  uint32_t* counters = split ? reinterpret_cast<uint32_t*>(ws) : nullptr;
   if (p.table)
-    return hip_status(q1::launch_gemv(p.g, x, x_ld, a, b, out, out_dtype, out_ld, partial, counters, s),
+    return hip_status(q1::launch_gemv(p.g, x, x_ld, a, b, out, out_dtype, out_ld, partial, s),
                       "packed kernel launch");
-  return hip_status(q1::launch_mma(p.m, x, x_ld, a, b, out, out_dtype, out_ld, partial, counters, s),
+  return hip_status(q1::launch_mma(p.m, x, x_ld, a, b, out, out_dtype, out_ld, partial, s),
                     "packed kernel launch");
 }
 

@@ -63,7 +63,6 @@ struct GemvPlan {
   int exact;             // every K range has exactly gemv_krmax(M) full chunks
   size_t lds_bytes;
   size_t partial_floats;  // KS > 1: KS*M*units
-  size_t counters;        // KS > 1: wgs_x
 };
 
 // Kernel arguments of one packed launch.
@@ -87,7 +86,6 @@ struct GemvArgs {
   void* out;
   int64_t out_ld;
   float* partial;
-  uint32_t* counters;
 };
 
 // Launch the packed kernel for M activation rows (defined in q1_gemv_m<M>.hip).
@@ -112,7 +110,6 @@ struct MmaPlan {
   int64_t wgs;     // S * P
   size_t lds_bytes;
   size_t partial_floats;  // S > 1: S*M*N*(pair ? 2 : 1)
-  size_t counters;        // S > 1: P
   int rb;                 // A rows per half in the LDS image: 8, or M (1, 2) for the compact image
 };
 
@@ -150,7 +147,7 @@ MmaArgs mma_args(const MmaPlan& plan, const uint16_t* x, int64_t x_ld, const QMa
                  int32_t out_dtype, int64_t out_ld, float* partial, uint32_t* counters);
 
 hipError_t launch_mma(const MmaPlan& plan, const uint16_t* x, int64_t x_ld, const QMat& a, const QMat* b, void* out,
-                      int32_t out_dtype, int64_t out_ld, float* partial, uint32_t* counters, hipStream_t stream);
+                      int32_t out_dtype, int64_t out_ld, float* partial, hipStream_t stream);
 
 // ---- single-launch FFN (q1_ffn.hip) ----------------------------------------
 
@@ -184,10 +181,9 @@ bool plan_gemv(int M, int64_t N, int64_t K, bool pair, bool affine, GemvPlan* pl
 // y (single) or h (pair) from packed weights.  `a` is the matrix for single
 // mode and gate for pair mode; `b` is up (pair mode) or ignored.
 // out_dtype: F32/BF16/F16 for single mode; pair mode always writes bf16 h.
-// partial/counters: workspace regions sized by the plan (may be null if KS==1).
+// partial: workspace region sized by the plan (may be null if KS==1).
 hipError_t launch_gemv(const GemvPlan& plan, const uint16_t* x, int64_t x_ld, const QMat& a, const QMat* b,
-                       void* out, int32_t out_dtype, int64_t out_ld, float* partial, uint32_t* counters,
-                       hipStream_t stream);
+                       void* out, int32_t out_dtype, int64_t out_ld, float* partial, hipStream_t stream);
 
 // Dequantise rows of `w` into out[T, K] (row r of the output is weight row
 // rows[r], or r when rows is null).  ids may be int32 or int64.

@@ -332,11 +332,6 @@ bool plan_gemv(int M, int64_t N, int64_t K, bool pair, bool affine, GemvPlan* p,
   p->units_per_wg = upw;
   p->wgs_x = (int)((p->units + upw - 1) / upw);
   p->partial_floats = (p->KS > 1) ? (size_t)p->KS * M * p->units : 0;
-  p->counters = (p->KS > 1) ? (size_t)p->wgs_x : 0;
-  if (p->counters * sizeof(uint32_t) > (size_t)kCounterBytes) {
-    *why = "too many workgroups for the arrival-counter region";
-    return false;
-  }
   return true;
 }
 
@@ -350,7 +345,7 @@ static hipError_t launch_reduce_m(const GemvPlan& plan, const GemvArgs& g, hipSt
 }
 
 hipError_t launch_gemv(const GemvPlan& plan, const uint16_t* x, int64_t x_ld, const QMat& a, const QMat* b, void* out,
-                       int32_t out_dtype, int64_t out_ld, float* partial, uint32_t* counters, hipStream_t stream) {
+                       int32_t out_dtype, int64_t out_ld, float* partial, hipStream_t stream) {
   GemvArgs g{};
   g.x = x;
   g.x_ld = x_ld;
@@ -376,7 +371,6 @@ hipError_t launch_gemv(const GemvPlan& plan, const uint16_t* x, int64_t x_ld, co
   g.out = out;
   g.out_ld = out_ld;
   g.partial = partial;
-  g.counters = counters;
   const bool affine = !a.symmetric;
   const bool mbf16 = a.meta_bf16 != 0;
   hipError_t e;

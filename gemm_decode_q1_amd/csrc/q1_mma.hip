@@ -129,7 +129,6 @@ bool plan_mma_split(int M, int64_t N, int64_t K, bool pair, bool affine, int S, 
   if (c->lds_bytes > 160 * 1024 - 64 || (int64_t)M * c->KSP * 16 > (int64_t)kPrepRounds * kThreads) return false;
   if ((int64_t)c->nb * 128 >= ((int64_t)1 << 22)) return false;  // result-slot index arithmetic
   c->partial_floats = c->S > 1 ? (size_t)c->S * M * N * nmat : 0;
-  c->counters = c->S > 1 ? (size_t)c->P : 0;  // per column p (P <= CUs); only the in-kernel handoff counts
   return true;
 }
 
@@ -213,8 +212,8 @@ MmaArgs mma_args(const MmaPlan& p, const uint16_t* x, int64_t x_ld, const QMat& 
 }
 
 hipError_t launch_mma(const MmaPlan& p, const uint16_t* x, int64_t x_ld, const QMat& a, const QMat* b, void* out,
-                      int32_t out_dtype, int64_t out_ld, float* partial, uint32_t* counters, hipStream_t s) {
-  const MmaArgs g = mma_args(p, x, x_ld, a, b, out, out_dtype, out_ld, partial, counters);
+                      int32_t out_dtype, int64_t out_ld, float* partial, hipStream_t s) {
+  const MmaArgs g = mma_args(p, x, x_ld, a, b, out, out_dtype, out_ld, partial, nullptr);
   const bool affine = !a.symmetric, mbf16 = a.meta_bf16 != 0, pair = b != nullptr;
   if (pair) {
     if (affine) return mbf16 ? launch_t<true, true, true>(p, g, s) : launch_t<true, false, true>(p, g, s);

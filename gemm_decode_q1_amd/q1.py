@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq1.so")
 
 Q1_F32, Q1_F16, Q1_BF16 = 0, 1, 2
-Q1_WS_RESERVED_BYTES = 16384  # arrival counters at the start of every workspace
+Q1_WS_RESERVED_BYTES = 16384  # reserved counter block at the start of every workspace
 _TORCH_TO_Q1 = {torch.float32: Q1_F32, torch.float16: Q1_F16, torch.bfloat16: Q1_BF16}
 _STATUS = {0: "Q1_OK", -1: "Q1_ERR_INVALID_ARG", -2: "Q1_ERR_UNSUPPORTED", -3: "Q1_ERR_WORKSPACE", -4: "Q1_ERR_HIP"}
 Q1_ERR_INVALID_ARG, Q1_ERR_UNSUPPORTED, Q1_ERR_WORKSPACE, Q1_ERR_HIP = -1, -2, -3, -4

@@ -50,13 +50,14 @@ typedef enum q1_status {
 
 typedef enum q1_dtype { Q1_F32 = 0, Q1_F16 = 1, Q1_BF16 = 2 } q1_dtype;
 
-/* The first Q1_WS_RESERVED_BYTES bytes of every workspace hold split-K
- * arrival counters.  They must be zero before a workspace is first used; every
- * call leaves them zero again once the stream has executed it, and no call
- * writes anything else there, with one exception: the single-launch q1_ffn
- * sets the last uint32 of the block (Q1_WS_STATUS_WORD, an index in uint32
- * units) to 1 if one of its waits gives up (see q1_ffn); nothing clears it but
- * the caller.  All other temporaries start after the block. */
+/* The first Q1_WS_RESERVED_BYTES bytes of every workspace are reserved for
+ * the arrival counters of the single-launch q1_ffn.  They must be zero before
+ * a workspace is first used; every call leaves them zero again once the stream
+ * has executed it, and no call writes anything else there, with one
+ * exception: the single-launch q1_ffn sets the last uint32 of the block
+ * (Q1_WS_STATUS_WORD, an index in uint32 units) to 1 if one of its waits gives
+ * up (see q1_ffn); nothing clears it but the caller.  All other temporaries
+ * start after the block. */
 #define Q1_WS_RESERVED_BYTES 16384
 #define Q1_WS_STATUS_WORD (Q1_WS_RESERVED_BYTES / 4 - 1)
 
