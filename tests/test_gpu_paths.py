@@ -157,3 +157,33 @@ def test_forced_table_ffn_pair(M):
     dh = np.abs(O.bf16_to_f32(_host(h)).astype(np.float64) - ref["h64"])
     assert (dh <= O.ffn_h_bound(ref)).all()
     assert O.check_within(_host(y), "bf16", ref["y"], O.ffn_y_bound(ref, _wd(d)))[0]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("meta,sym", [("f16", True), ("bf16", False)])
+def test_ffn_pair_split_k(M, meta, sym):
+    """Gate/up pairs whose K (H = 9216) does not fit one workgroup's LDS image:
+    the pair is split along K and the reduce launch adds the segments and
+    applies SiLU * mul (the table kernel's own split reduction at M = 1).  h
+    and y checked against the oracle on every element."""
+    H, I, Ho = 9216, 640, 384
+    rng = np.random.Generator(np.random.PCG64(500 + M))
+    g = S.draw_weight(rng, I, H, meta, sym)
+    u = S.draw_weight(rng, I, H, meta, sym)
+    d = S.draw_weight(rng, Ho, I, meta, sym)
+    x = S.draw_x(rng, M, H)
+    W = [Q.PackedQ1.from_host(t) for t in (g, u, d)]
+    # the partial sums need workspace beyond the counter block and h
+    assert Q.q1_ffn_workspace_bytes(M, *W) > 16384 + M * I * 2 + 256
+    _say(f"ffn pair split K M={M} H={H} {meta} sym={sym}")
+    y, h = Q.q1_ffn(_x_dev(x), *W, return_hidden=True)
+    ref = O.ffn_ref(x, _wd(g), _wd(u), _wd(d))
+    dh = np.abs(O.bf16_to_f32(_host(h)).astype(np.float64) - ref["h64"])
+    hb = O.ffn_h_bound(ref)
+    _say(f"  h worst ratio {np.max(dh / hb):.3e}")
+    assert (dh <= hb).all()
+    y_h, A_h = O.qmm_ref(_host(h), **_wd(d))
+    ok, ratio, nbad = O.check_close(_host(y), "bf16", y_h, A_h)
+    _say(f"  y (on gpu h) worst ratio {ratio:.3e}")
+    assert ok, nbad
+    assert O.check_within(_host(y), "bf16", ref["y"], O.ffn_y_bound(ref, _wd(d)))[0]
