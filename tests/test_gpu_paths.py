@@ -187,3 +187,57 @@ def test_ffn_pair_split_k(M, meta, sym):
     _say(f"  y (on gpu h) worst ratio {ratio:.3e}")
     assert ok, nbad
     assert O.check_within(_host(y), "bf16", ref["y"], O.ffn_y_bound(ref, _wd(d)))[0]
+
+
+GRAPH_CASES = [  # (label, M, N, K, meta, symmetric, Q1_PACKED_KERNEL)
+    ("mma", 4, 1040, 5120, "f16", True, None),
+    ("mma_split", 3, 520, 17408, "bf16", False, None),
+    ("mma_one_row_split", 1, 1000, 9216, "f16", True, None),
+    ("table_split", 1, 1000, 9216, "f16", True, "table"),
+    ("mma_two_rows", 2, 700, 3072, "bf16", True, None),
+    ("wide", 40, 600, 2048, "f16", True, None),
+]
+
+
+@pytest.mark.parametrize("case", GRAPH_CASES, ids=lambda c: c[0])
+def test_qmm_replays_in_a_graph(case):
+    """q1_qmm captured once in a HIP graph (with its reduce or image launch)
+    and replayed four times, with eager changes to x and an eager call on a
+    second workspace between the replays: every replay equals the eager call
+    on the same x bit for bit, and the first is within the oracle's bound."""
+    label, M, N, K, meta, sym, kernel = case
+    if kernel is None:
+        _qmm_graph_case(label, M, N, K, meta, sym)
+    else:
+        with _env("Q1_PACKED_KERNEL", kernel):
+            _qmm_graph_case(label, M, N, K, meta, sym)
+
+
+def _qmm_graph_case(label, M, N, K, meta, sym):
+    rng = np.random.Generator(np.random.PCG64(600 + M))
+    w = S.draw_weight(rng, N, K, meta, sym)
+    W = Q.PackedQ1.from_host(w)
+    xd = _x_dev(S.draw_x(rng, M, K))
+    need = Q.q1_qmm_workspace_bytes(M, W)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    ws_eager = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    _say(f"graph replay {label}: M={M} N={N} K={K} {meta} sym={sym} workspace {need}")
+    Q.q1_qmm(xd, W, torch.float32, y=y, workspace=ws)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        Q.q1_qmm(xd, W, torch.float32, y=y, workspace=ws)
+    for step in range(4):
+        if step > 0:
+            xd.copy_(_x_dev(S.draw_x(rng, M, K)))
+        graph.replay()
+        torch.cuda.synchronize()
+        y_eager = Q.q1_qmm(xd, W, torch.float32, workspace=ws_eager)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y_eager.view(torch.int32)), step
+        if step == 0:
+            ref, A = O.qmm_ref(_host(xd), **_wd(w))
+            ok, ratio, nbad = O.check_close(_host(y), "f32", ref, A)
+            _say(f"  worst err/bound {ratio:.3e}")
+            assert ok, nbad
