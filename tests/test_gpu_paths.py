@@ -241,3 +241,33 @@ def _qmm_graph_case(label, M, N, K, meta, sym):
             ok, ratio, nbad = O.check_close(_host(y), "f32", ref, A)
             _say(f"  worst err/bound {ratio:.3e}")
             assert ok, nbad
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_ffn_replays_in_a_graph(M):
+    """The two-launch q1_ffn (gate/up pair, then a down projection split
+    along K = 9216 with its reduce launch) captured in a HIP graph and
+    replayed four times with eager changes to x between replays: every replay
+    equals an eager call bit for bit."""
+    H, I, Ho = 1024, 9216, 500
+    rng = np.random.Generator(np.random.PCG64(700 + M))
+    W = [Q.PackedQ1.from_host(S.draw_weight(rng, n, k, "f16", True)) for n, k in ((I, H), (I, H), (Ho, I))]
+    xd = _x_dev(S.draw_x(rng, M, H))
+    need = Q.q1_ffn_workspace_bytes(M, *W)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws_eager = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    y = torch.empty(M, Ho, dtype=torch.bfloat16, device="cuda")
+    _say(f"ffn graph replay M={M}")
+    Q.q1_ffn(xd, *W, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        Q.q1_ffn(xd, *W, y=y, workspace=ws)
+    for step in range(4):
+        if step > 0:
+            xd.copy_(_x_dev(S.draw_x(rng, M, H)))
+        graph.replay()
+        torch.cuda.synchronize()
+        y_eager = Q.q1_ffn(xd, *W, workspace=ws_eager)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_eager.view(torch.int16)), step
