@@ -21,8 +21,8 @@
 //   has the fewest items).  A unit (segment, column p) issues its first weight loads,
 //   then waits until its segment's counter shows every phase-1 tile of the
 //   segment, takes one agent-scope acquire, and converts its part of h; the
-//   segments' partial sums meet as in the split matmul (the last arrival per
-//   column adds them in segment order).
+//   segments' partial sums meet in the stage's in-kernel handoff (HANDOFF in
+//   q1_mma_stage.h: the last arrival per column adds them in segment order).
 //
 // Every phase-1 tile is owned by a workgroup of the same grid, and the grid
 // is one workgroup per compute unit, so all producers are resident and the
@@ -34,7 +34,7 @@
 // counter, so a call leaves the counter block as it found it.
 //
 // Measured at hidden 5120, intermediate 17408 (fp16 symmetric, M = 1..8):
-// 33-48 us against 20-26 us for the pair launch followed by the down launch,
+// 32-39 us against 18-24 us for the pair launch followed by the down launch,
 // which therefore stays the default (this launch is selected by
 // Q1_FFN_KERNEL=single).  Per-workgroup timestamps show why: the agent-scope
 // release that publishes h is an L2 write-back, which under the weight stream
