@@ -14,8 +14,8 @@ LIB = os.path.join(PKG, "libq1.so")
 SOURCES = ([os.path.join(PKG, "csrc", "q1_api.cpp"), os.path.join(PKG, "csrc", "q1_kernels.hip"),
             os.path.join(PKG, "csrc", "q1_mma.hip"), os.path.join(PKG, "csrc", "q1_ffn.hip"),
             os.path.join(PKG, "csrc", "q1_wide.hip"),
-            os.path.join(PKG, "csrc", "q1_meta.hip"), os.path.join(PKG, "csrc", "q1_scratch.hip")] +
-           [os.path.join(PKG, "csrc", f"q1_gemv_m{m}.hip") for m in range(1, 9)])
+            os.path.join(PKG, "csrc", "q1_meta.hip"), os.path.join(PKG, "csrc", "q1_scratch.hip"),
+            os.path.join(PKG, "csrc", "q1_gemv.hip")])
 # Packed-FP32 instructions are disabled for all device code (see the design
 # notes): hipcc otherwise forms v_pk_*_f32 from plain float code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",

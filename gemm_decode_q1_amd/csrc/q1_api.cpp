@@ -117,7 +117,7 @@ q1_status hip_status(hipError_t e, const char* what) {
 // untouched); a packed launch's fp32 partial sums go at `base`.
 constexpr size_t kReserved = Q1_WS_RESERVED_BYTES;
 
-// Packed narrow-M launches: the nibble-table kernel (q1_gemv.inc) for one
+// Packed narrow-M launches: the nibble-table kernel (q1_gemv.hip) for one
 // activation row, the matrix-core kernel (q1_mma.hip) for 2..8 rows, where
 // table lookups grow with the row count.  Q1_PACKED_KERNEL=table|mma forces
 // one of them for every row count (read on every call, like

@@ -1,12 +1,11 @@
-// Packed narrow-M Q1 matmul kernel template; included once per M by
-// q1_gemv_m<M>.hip so the eight row counts compile in parallel.
+// Packed narrow-M Q1 matmul: the nibble-table kernel (the default for one
+// activation row; 2..8 rows when the matrix-core plan rejects a shape or
+// Q1_PACKED_KERNEL=table), instantiated for M = 1..8 at the end.
 //
 // y[m][n] = sum_k x[m][k] * w[n][k],  w = scale*bit + bias (symmetric:
 // bias = -scale/2), for M <= 8 activation rows (Higgs PR #212, "What": narrow
 // Q1 matmuls stay packed; rMLX issue #207: 32 weights per uint32, LSB first,
 // one scale/bias per 128 weights).
-#pragma once
-
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -392,5 +391,14 @@ hipError_t launch_gemv_m(const GemvPlan& plan, const GemvArgs& args, bool affine
   if (affine) return mbf16 ? launch_gemv_e<M, true, true>(plan, args, stream) : launch_gemv_e<M, true, false>(plan, args, stream);
   return mbf16 ? launch_gemv_e<M, false, true>(plan, args, stream) : launch_gemv_e<M, false, false>(plan, args, stream);
 }
+
+template hipError_t launch_gemv_m<1>(const GemvPlan&, const GemvArgs&, bool, bool, hipStream_t);
+template hipError_t launch_gemv_m<2>(const GemvPlan&, const GemvArgs&, bool, bool, hipStream_t);
+template hipError_t launch_gemv_m<3>(const GemvPlan&, const GemvArgs&, bool, bool, hipStream_t);
+template hipError_t launch_gemv_m<4>(const GemvPlan&, const GemvArgs&, bool, bool, hipStream_t);
+template hipError_t launch_gemv_m<5>(const GemvPlan&, const GemvArgs&, bool, bool, hipStream_t);
+template hipError_t launch_gemv_m<6>(const GemvPlan&, const GemvArgs&, bool, bool, hipStream_t);
+template hipError_t launch_gemv_m<7>(const GemvPlan&, const GemvArgs&, bool, bool, hipStream_t);
+template hipError_t launch_gemv_m<8>(const GemvPlan&, const GemvArgs&, bool, bool, hipStream_t);
 
 }  // namespace q1

@@ -88,7 +88,7 @@ struct GemvArgs {
   float* partial;
 };
 
-// Launch the packed kernel for M activation rows (defined in q1_gemv_m<M>.hip).
+// Launch the packed kernel for M activation rows (q1_gemv.hip).
 template <int M>
 hipError_t launch_gemv_m(const GemvPlan& plan, const GemvArgs& args, bool affine, bool mbf16, hipStream_t stream);
 
